@@ -1,0 +1,610 @@
+// C ABI of libcgtp (declared in include/cgtp.h): plan construction (irreps parser,
+// path enumerator, real-CG tables, wave-job scheduler), argument validation and the
+// launch sequence of the neighbour list, mask prepare, edge harmonics and the fused
+// convolution.  No allocation happens outside cgtp_plan_create.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cgtp.h"
+#include "launch.hpp"
+#include "variants.hpp"
+
+namespace cgtp {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CGTP_OK;
+}
+
+#define CGTP_HIP(call)                                                                  \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(CGTP_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+struct Irrep {
+  int mul, l, p;
+};
+
+struct PathInfo {
+  int l1, p1, l2, p2, l3, p3, mul, i_in, i_sh, in_off, out_off, w_off;
+};
+
+// Parse "128x0e+64x1o" (a bare "1o" means multiplicity 1).
+bool parse_irreps(const char* spec, std::vector<Irrep>& out, std::string& err) {
+  out.clear();
+  if (!spec || !*spec) {
+    err = "empty irreps spec";
+    return false;
+  }
+  std::string s;
+  for (const char* c = spec; *c; ++c)
+    if (*c != ' ') s.push_back(*c);
+  size_t pos = 0;
+  while (true) {
+    size_t plus = s.find('+', pos);
+    std::string term = s.substr(pos, plus == std::string::npos ? std::string::npos : plus - pos);
+    if (term.empty()) {
+      err = "empty term in '" + s + "'";
+      return false;
+    }
+    long mul = 1;
+    std::string ir = term;
+    size_t x = term.find('x');
+    if (x != std::string::npos) {
+      std::string m = term.substr(0, x);
+      if (m.empty() || m.find_first_not_of("0123456789") != std::string::npos || m.size() > 9) {
+        err = "bad multiplicity in '" + term + "'";
+        return false;
+      }
+      mul = std::stol(m);
+      ir = term.substr(x + 1);
+    }
+    if (ir.size() < 2 || (ir.back() != 'e' && ir.back() != 'o')) {
+      err = "bad irrep '" + term + "'";
+      return false;
+    }
+    std::string ls = ir.substr(0, ir.size() - 1);
+    if (ls.empty() || ls.find_first_not_of("0123456789") != std::string::npos || ls.size() > 4) {
+      err = "bad irrep '" + term + "'";
+      return false;
+    }
+    out.push_back(Irrep{int(mul), std::stoi(ls), ir.back() == 'e' ? 1 : -1});
+    if (plus == std::string::npos) break;
+    pos = plus + 1;
+  }
+  return true;
+}
+
+std::string format_irreps(const std::vector<Irrep>& v) {
+  std::string s;
+  for (size_t k = 0; k < v.size(); ++k) {
+    if (k) s += "+";
+    s += std::to_string(v[k].mul) + "x" + std::to_string(v[k].l) + (v[k].p == 1 ? "e" : "o");
+  }
+  return s;
+}
+
+int sign_pow(int l) { return (l % 2 == 0) ? 1 : -1; }
+
+// Real CG of a path as a dense fp32 table (run-time evaluation of the same
+// constexpr formulas the kernels are specialised with).
+void dense_cg(int l1, int l2, int l3, std::vector<float>& out) {
+  const int n1 = 2 * l1 + 1, n2 = 2 * l2 + 1, n3 = 2 * l3 + 1;
+  out.assign(size_t(n1) * n2 * n3, 0.0f);
+  for (int a = 0; a < n1; ++a)
+    for (int b = 0; b < n2; ++b)
+      for (int c = 0; c < n3; ++c) {
+        double v = real_cg(l1, l2, l3, a - l1, b - l2, c - l3);
+        if (v < 1e-12 && v > -1e-12) v = 0.0;
+        out[(size_t(a) * n2 + b) * n3 + c] = float(v);
+      }
+}
+
+int next_pow2(int v) {
+  int p = 1;
+  while (p < v) p <<= 1;
+  return p;
+}
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+}  // namespace
+}  // namespace cgtp
+
+using namespace cgtp;
+
+struct cgtp_plan_s {
+  std::vector<Irrep> in, sh, out;
+  std::vector<PathInfo> paths;
+  int64_t f_in = 0, f_out = 0, w = 0;
+  int l_sh_max = 0;
+  int sh_stride = 1;
+  std::string irreps_out;
+  std::vector<Job> jobs;             // grouped by kernel class, heavy jobs first
+  std::vector<int> class_begin;      // [kNumClasses + 1]
+  int n_variants = 0;
+  bool host_only = true;
+  int device = -1;
+  Job* d_jobs = nullptr;
+};
+
+namespace {
+
+// Wave-job schedule.  Per path: K = 4 channels per lane when every offset and stride
+// is 16-byte aligned, else K = 1; lanes per node = next power of two of mul/K, at most
+// 64 (larger multiplicities are cut into channel blocks of 64*K).  Jobs are grouped by
+// kernel class and ordered by per-edge cost, heaviest first (LunaTP Table 9: ordering
+// by descending CG-term count was fastest).
+void schedule(cgtp_plan_s& P) {
+  P.jobs.clear();
+  struct Tmp {
+    Job j;
+    int cls;
+    double cost;
+  };
+  std::vector<Tmp> tmp;
+  std::vector<int> used(kNumVariants, 0);
+  const bool strides4 = (P.f_in % 4 == 0) && (P.f_out % 4 == 0) && (P.w % 4 == 0);
+  for (size_t pi = 0; pi < P.paths.size(); ++pi) {
+    const PathInfo& p = P.paths[pi];
+    const bool al = strides4 && p.mul % 4 == 0 && p.in_off % 4 == 0 && p.out_off % 4 == 0 && p.w_off % 4 == 0;
+    const int K = al ? 4 : 1;
+    const int v = variant_index(p.l1, p.l2, p.l3, K);
+    used[v] = 1;
+    std::vector<float> cg;
+    dense_cg(p.l1, p.l2, p.l3, cg);
+    const int n1 = 2 * p.l1 + 1, n2 = 2 * p.l2 + 1, n3 = 2 * p.l3 + 1;
+    int nnz_c = 0, nnz_a = 0;
+    for (int a = 0; a < n1; ++a)
+      for (int c = 0; c < n3; ++c) {
+        bool any = false;
+        for (int b = 0; b < n2; ++b)
+          if (cg[(size_t(a) * n2 + b) * n3 + c] != 0.0f) {
+            ++nnz_c;
+            any = true;
+          }
+        nnz_a += any;
+      }
+    const double cost = nnz_c + K * (nnz_a + std::min(n1, n3));
+    const int block = 64 * K;
+    for (int c0 = 0; c0 < p.mul; c0 += block) {
+      const int n_ch = std::min(block, p.mul - c0);
+      const int lanes = next_pow2((n_ch + K - 1) / K);
+      Job j{};
+      j.variant = v;
+      j.lanes_log2 = ilog2(lanes);
+      j.n_ch = n_ch;
+      j.in_off = p.in_off + c0 * n1;
+      j.out_off = p.out_off + c0 * n3;
+      j.w_off = p.w_off + c0;
+      j.sh_off = p.l2 * p.l2;
+      j.path = int(pi);
+      tmp.push_back(Tmp{j, variant_class(v), cost});
+    }
+  }
+  std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& a, const Tmp& b) {
+    if (a.cls != b.cls) return a.cls < b.cls;
+    return a.cost > b.cost;
+  });
+  P.class_begin.assign(kNumClasses + 1, 0);
+  for (const Tmp& t : tmp) {
+    P.jobs.push_back(t.j);
+    P.class_begin[t.cls + 1]++;
+  }
+  for (int c = 0; c < kNumClasses; ++c) P.class_begin[c + 1] += P.class_begin[c];
+  P.n_variants = 0;
+  for (int u : used) P.n_variants += u;
+}
+
+int tasks_of(const Job& j, int64_t n) {
+  const int s = 64 >> j.lanes_log2;
+  return int((n + s - 1) / s);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct FwdWorkspace {
+  int32_t *act_row_ptr, *act_eid, *act_col, *order, *deg, *tmp_a, *tmp_b, *task_start;
+  float* sh;
+  size_t bytes;
+};
+
+FwdWorkspace carve(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
+  FwdWorkspace w{};
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.act_row_ptr = reinterpret_cast<int32_t*>(take(size_t(n + 1) * 4));
+  w.act_eid = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
+  w.act_col = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
+  w.order = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.deg = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.tmp_a = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.tmp_b = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.task_start = reinterpret_cast<int32_t*>(take((P.jobs.size() + 1) * 4));
+  w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_stride) * 4));
+  w.bytes = off;
+  return w;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_device(const cgtp_plan_s* P) {
+  int dev = -1;
+  CGTP_HIP(hipGetDevice(&dev));
+  if (dev != P->device) return fail(CGTP_ERR_INVALID_ARG, "plan was created on device %d, current device is %d", P->device, dev);
+  return CGTP_OK;
+}
+
+const int kMaxInt32 = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+const char* cgtp_last_error(void) { return g_last_error.c_str(); }
+
+const char* cgtp_version(void) { return "cgtp 0.1 gfx950"; }
+
+int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max, int path_rule,
+                     unsigned flags, cgtp_plan_t* out) {
+  if (!out) return fail(CGTP_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (path_rule != CGTP_PATHS_ALL && path_rule != CGTP_PATHS_PARITY)
+    return fail(CGTP_ERR_INVALID_ARG, "unknown path rule %d", path_rule);
+  if (flags & ~unsigned(CGTP_PLAN_HOST_ONLY)) return fail(CGTP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (l_out_max < 0) return fail(CGTP_ERR_INVALID_ARG, "l_out_max < 0");
+  auto P = new cgtp_plan_s();
+  std::string err;
+  if (!parse_irreps(irreps_in, P->in, err) || !parse_irreps(irreps_sh, P->sh, err)) {
+    delete P;
+    return fail(CGTP_ERR_PARSE, "%s", err.c_str());
+  }
+  for (const Irrep& r : P->in)
+    if (r.l > kMaxL || r.mul <= 0) {
+      delete P;
+      return fail(CGTP_ERR_UNSUPPORTED, "input irrep %dx%d: need l <= %d and mul > 0", r.mul, r.l, kMaxL);
+    }
+  for (const Irrep& r : P->sh)
+    if (r.l > kMaxL || r.mul != 1) {
+      delete P;
+      return fail(CGTP_ERR_UNSUPPORTED, "edge SH irrep %dx%d: need l <= %d and multiplicity 1", r.mul, r.l, kMaxL);
+    }
+  std::vector<int> in_off;
+  int64_t off = 0;
+  for (const Irrep& r : P->in) {
+    in_off.push_back(int(off));
+    off += int64_t(r.mul) * (2 * r.l + 1);
+  }
+  P->f_in = off;
+  struct Raw {
+    int l1, p1, l2, p2, l3, p3, mul, i_in, i_sh;
+  };
+  std::vector<Raw> raw;
+  for (size_t a = 0; a < P->in.size(); ++a)
+    for (size_t b = 0; b < P->sh.size(); ++b) {
+      const Irrep &x = P->in[a], &y = P->sh[b];
+      const int lo = std::abs(x.l - y.l), hi = std::min(x.l + y.l, l_out_max);
+      for (int l3 = lo; l3 <= hi; ++l3) {
+        const int p3 = x.p * y.p;
+        if (path_rule == CGTP_PATHS_PARITY && p3 != sign_pow(l3)) continue;
+        raw.push_back(Raw{x.l, x.p, y.l, y.p, l3, p3, x.mul, int(a), int(b)});
+      }
+    }
+  if (raw.empty()) {
+    delete P;
+    return fail(CGTP_ERR_UNSUPPORTED, "no path survives the path rule");
+  }
+  // output irreps sorted by (l3, e before o); path blocks in path order
+  std::vector<std::pair<int, int>> keys;
+  for (const Raw& r : raw) keys.emplace_back(r.l3, r.p3 == 1 ? 0 : 1);
+  std::sort(keys.begin(), keys.end());
+  keys.erase(std::unique(keys.begin(), keys.end()), keys.end());
+  std::vector<int> out_off(raw.size()), w_off(raw.size());
+  int64_t fo = 0, ch = 0;
+  for (auto& k : keys) {
+    const int l3 = k.first, p3 = k.second == 0 ? 1 : -1;
+    int64_t c_in = 0;
+    for (size_t q = 0; q < raw.size(); ++q)
+      if (raw[q].l3 == l3 && raw[q].p3 == p3) {
+        out_off[q] = int(fo + c_in * (2 * l3 + 1));
+        w_off[q] = int(ch + c_in);
+        c_in += raw[q].mul;
+      }
+    P->out.push_back(Irrep{int(c_in), l3, p3});
+    fo += c_in * (2 * l3 + 1);
+    ch += c_in;
+  }
+  P->f_out = fo;
+  P->w = ch;
+  if (P->f_in > kMaxInt32 || P->f_out > kMaxInt32) {
+    delete P;
+    return fail(CGTP_ERR_UNSUPPORTED, "feature width exceeds int32");
+  }
+  for (size_t q = 0; q < raw.size(); ++q) {
+    const Raw& r = raw[q];
+    P->paths.push_back(PathInfo{r.l1, r.p1, r.l2, r.p2, r.l3, r.p3, r.mul, r.i_in, r.i_sh, in_off[r.i_in],
+                                out_off[q], w_off[q]});
+  }
+  P->l_sh_max = 0;
+  for (const Irrep& r : P->sh) P->l_sh_max = std::max(P->l_sh_max, r.l);
+  P->sh_stride = (P->l_sh_max + 1) * (P->l_sh_max + 1);
+  P->irreps_out = format_irreps(P->out);
+  schedule(*P);
+
+  P->host_only = (flags & CGTP_PLAN_HOST_ONLY) != 0;
+  if (!P->host_only) {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+      delete P;
+      return fail(CGTP_ERR_NO_DEVICE, "no HIP device");
+    }
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      delete P;
+      return fail(CGTP_ERR_NO_DEVICE, "current device is not gfx950");
+    }
+    P->device = dev;
+    const size_t bytes = P->jobs.size() * sizeof(Job);
+    hipError_t e = hipMalloc(&P->d_jobs, bytes);
+    if (e == hipSuccess) e = hipMemcpy(P->d_jobs, P->jobs.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      if (P->d_jobs) (void)hipFree(P->d_jobs);
+      delete P;
+      return fail(CGTP_ERR_HIP, "job table upload: %s", hipGetErrorString(e));
+    }
+  }
+  *out = P;
+  return ok();
+}
+
+void cgtp_plan_destroy(cgtp_plan_t plan) {
+  if (!plan) return;
+  if (plan->d_jobs) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != plan->device) (void)hipSetDevice(plan->device);
+    (void)hipFree(plan->d_jobs);
+    if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
+  }
+  delete plan;
+}
+
+int cgtp_plan_info(cgtp_plan_t P, int64_t* f_in, int64_t* f_out, int64_t* w_per_edge, int* n_paths,
+                   int* l_sh_max, char* irreps_out, size_t cap) {
+  if (!P) return fail(CGTP_ERR_INVALID_ARG, "plan is NULL");
+  if (f_in) *f_in = P->f_in;
+  if (f_out) *f_out = P->f_out;
+  if (w_per_edge) *w_per_edge = P->w;
+  if (n_paths) *n_paths = int(P->paths.size());
+  if (l_sh_max) *l_sh_max = P->l_sh_max;
+  if (irreps_out && cap > 0) {
+    std::strncpy(irreps_out, P->irreps_out.c_str(), cap - 1);
+    irreps_out[cap - 1] = '\0';
+  }
+  return ok();
+}
+
+int cgtp_plan_paths(cgtp_plan_t P, int32_t* rows) {
+  if (!P || !rows) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  for (size_t k = 0; k < P->paths.size(); ++k) {
+    const PathInfo& p = P->paths[k];
+    const int32_t r[10] = {p.l1, p.p1, p.l2, p.p2, p.l3, p.p3, p.mul, p.in_off, p.out_off, p.w_off};
+    std::memcpy(rows + 10 * k, r, sizeof(r));
+  }
+  return ok();
+}
+
+int cgtp_plan_cg(cgtp_plan_t P, int path, float* dense) {
+  if (!P || !dense) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  if (path < 0 || size_t(path) >= P->paths.size()) return fail(CGTP_ERR_INVALID_ARG, "path %d out of range", path);
+  const PathInfo& p = P->paths[path];
+  std::vector<float> t;
+  dense_cg(p.l1, p.l2, p.l3, t);
+  std::memcpy(dense, t.data(), t.size() * sizeof(float));
+  return ok();
+}
+
+int cgtp_plan_schedule(cgtp_plan_t P, int* n_jobs, int* n_variants) {
+  if (!P) return fail(CGTP_ERR_INVALID_ARG, "plan is NULL");
+  if (n_jobs) *n_jobs = int(P->jobs.size());
+  if (n_variants) *n_variants = P->n_variants;
+  return ok();
+}
+
+int cgtp_workspace_size(cgtp_plan_t P, int64_t n_nodes, int64_t n_edges, int has_mask, size_t* bytes) {
+  (void)has_mask;
+  if (!P || !bytes) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  if (n_nodes < 0 || n_edges < 0) return fail(CGTP_ERR_INVALID_ARG, "negative size");
+  *bytes = carve(*P, n_nodes, n_edges, nullptr).bytes;
+  return ok();
+}
+
+int cgtp_neighbors_workspace_size(int64_t n_nodes, const float box[3], float cutoff, size_t* bytes) {
+  if (!box || !bytes) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  if (n_nodes < 0 || n_nodes > kMaxInt32 - 1) return fail(CGTP_ERR_INVALID_ARG, "bad n_nodes");
+  if (!(cutoff > 0.0f) || !(box[0] > 0.0f) || !(box[1] > 0.0f) || !(box[2] > 0.0f))
+    return fail(CGTP_ERR_INVALID_ARG, "box and cutoff must be positive");
+  *bytes = nbr_workspace_bytes(n_nodes, make_nbr_grid(n_nodes, box, cutoff));
+  return ok();
+}
+
+int cgtp_neighbors_build(const float* pos, int64_t n_nodes, const float box[3], float cutoff, int32_t* row_ptr,
+                         int32_t* col, int8_t* shift, int64_t edge_capacity, int64_t* n_edges, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  if (!box || !row_ptr || !n_edges) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  if (n_nodes < 0 || n_nodes > kMaxInt32 - 1) return fail(CGTP_ERR_INVALID_ARG, "bad n_nodes");
+  if (n_nodes > 0 && !pos) return fail(CGTP_ERR_INVALID_ARG, "pos is NULL");
+  if (edge_capacity < 0) return fail(CGTP_ERR_INVALID_ARG, "negative edge capacity");
+  if (!(cutoff > 0.0f) || !(box[0] > 0.0f) || !(box[1] > 0.0f) || !(box[2] > 0.0f))
+    return fail(CGTP_ERR_INVALID_ARG, "box and cutoff must be positive");
+  if (!aligned(pos, 4) || !aligned(row_ptr, 4) || !aligned(col, 4))
+    return fail(CGTP_ERR_INVALID_ARG, "misaligned pointer");
+  const NbrGrid g = make_nbr_grid(n_nodes, box, cutoff);
+  const size_t need = nbr_workspace_bytes(n_nodes, g);
+  if (!workspace || ws_bytes < need)
+    return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(CGTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const NbrWorkspace w = carve_nbr_workspace(workspace, n_nodes, g);
+  CGTP_HIP(launch_nbr_count(pos, int(n_nodes), g, w, row_ptr, s));
+  int32_t e_host = 0;
+  CGTP_HIP(hipMemcpyAsync(&e_host, row_ptr + n_nodes, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  CGTP_HIP(hipStreamSynchronize(s));
+  *n_edges = e_host;
+  if (e_host > edge_capacity)
+    return fail(CGTP_ERR_CAPACITY, "edge list needs %d entries, capacity is %lld", e_host, (long long)edge_capacity);
+  if (e_host > 0) {
+    if (!col || !shift) return fail(CGTP_ERR_INVALID_ARG, "col/shift NULL with edges present");
+    CGTP_HIP(launch_nbr_fill(pos, int(n_nodes), g, w, row_ptr, col, shift, s));
+  }
+  return ok();
+}
+
+static int check_graph_args(const cgtp_plan_s* P, int64_t n_nodes, int64_t n_edges, const int32_t* row_ptr) {
+  if (!P) return fail(CGTP_ERR_INVALID_ARG, "plan is NULL");
+  if (P->host_only) return fail(CGTP_ERR_INVALID_ARG, "plan was created with CGTP_PLAN_HOST_ONLY");
+  if (n_nodes < 0 || n_edges < 0) return fail(CGTP_ERR_INVALID_ARG, "negative size");
+  if (n_nodes > kMaxInt32 - 1 || n_edges > kMaxInt32 - 1) return fail(CGTP_ERR_INVALID_ARG, "size exceeds int32");
+  if (!row_ptr) return fail(CGTP_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (!aligned(row_ptr, 4)) return fail(CGTP_ERR_INVALID_ARG, "misaligned row_ptr");
+  return check_device(P);
+}
+
+int cgtp_conv_prepare(cgtp_plan_t P, const int32_t* row_ptr, const uint8_t* mask, int64_t n_nodes, int64_t n_edges,
+                      int32_t* act_row_ptr, int32_t* act_eid, int32_t* order, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
+  if (rc != CGTP_OK) return rc;
+  if (!act_row_ptr || !order || (n_edges > 0 && !act_eid)) return fail(CGTP_ERR_INVALID_ARG, "NULL output");
+  const FwdWorkspace w = carve(*P, n_nodes, n_edges, workspace);
+  if (!workspace || ws_bytes < w.bytes)
+    return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, w.bytes);
+  if (!aligned(workspace, 256)) return fail(CGTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  CGTP_HIP(launch_prepare_rows(row_ptr, mask, int(n_nodes), w.deg, act_row_ptr, order, w.tmp_a, w.tmp_b, s));
+  EdgeGeom g{};
+  g.row_ptr = row_ptr;
+  g.mask = mask;
+  g.act_row_ptr = act_row_ptr;
+  g.n_nodes = int(n_nodes);
+  g.n_edges = int(n_edges);
+  CGTP_HIP(launch_edge_pass(g, act_eid, nullptr, nullptr, P->l_sh_max, s));
+  return ok();
+}
+
+static void fill_cell(EdgeGeom& g, const float* cell) {
+  g.has_cell = cell != nullptr;
+  for (int k = 0; k < 9; ++k) g.cell[k] = cell ? double(cell[k]) : 0.0;
+}
+
+int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
+                 const int32_t* col, const int8_t* shift, int64_t n_edges, float* sh, void* stream) {
+  int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
+  if (rc != CGTP_OK) return rc;
+  if (n_edges > 0 && (!pos || !col || !sh)) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  EdgeGeom g{};
+  g.pos = pos;
+  g.row_ptr = row_ptr;
+  g.col = col;
+  g.shift = shift;
+  g.act_row_ptr = row_ptr;
+  g.n_nodes = int(n_nodes);
+  g.n_edges = int(n_edges);
+  fill_cell(g, cell);
+  CGTP_HIP(launch_edge_pass(g, nullptr, nullptr, sh, P->l_sh_max, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
+                      const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
+                      const uint8_t* mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
+  if (rc != CGTP_OK) return rc;
+  if (n_nodes > 0 && (!out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
+  if (n_edges > 0 && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(col, 4))
+    return fail(CGTP_ERR_INVALID_ARG, "x, w and out must be 16-byte aligned");
+  const FwdWorkspace ws = carve(*P, n_nodes, n_edges, workspace);
+  if (!workspace || ws_bytes < ws.bytes)
+    return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, ws.bytes);
+  if (!aligned(workspace, 256)) return fail(CGTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (n_nodes == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // 1. active CSR and node order (BranchIP sparse evaluation; LunaTP Table 9)
+  CGTP_HIP(launch_prepare_rows(row_ptr, mask, int(n_nodes), ws.deg, ws.act_row_ptr, ws.order, ws.tmp_a, ws.tmp_b, s));
+  // 2. compacted active edges and their harmonics
+  EdgeGeom g{};
+  g.pos = pos;
+  g.row_ptr = row_ptr;
+  g.col = col;
+  g.shift = shift;
+  g.mask = mask;
+  g.act_row_ptr = ws.act_row_ptr;
+  g.n_nodes = int(n_nodes);
+  g.n_edges = int(n_edges);
+  fill_cell(g, cell);
+  CGTP_HIP(launch_edge_pass(g, ws.act_eid, ws.act_col, ws.sh, P->l_sh_max, s));
+  // 3. wave-task prefix of all jobs for this node count
+  CGTP_HIP(launch_task_prefix(P->d_jobs, int(P->jobs.size()), int(n_nodes), ws.task_start, s));
+  // 4. the fused convolution, one launch per kernel class present in the plan
+  ConvArgs a{};
+  a.x = x;
+  a.w = w;
+  a.sh = ws.sh;
+  a.act_row_ptr = ws.act_row_ptr;
+  a.act_eid = ws.act_eid;
+  a.act_col = ws.act_col;
+  a.order = ws.order;
+  a.out = out;
+  a.n_nodes = int(n_nodes);
+  a.f_in = int(P->f_in);
+  a.f_out = int(P->f_out);
+  a.w_stride = int(P->w);
+  a.sh_stride = P->sh_stride;
+  for (int c = 0; c < kNumClasses; ++c) {
+    const int b = P->class_begin[c], e = P->class_begin[c + 1];
+    if (b == e) continue;
+    int64_t tasks = 0;
+    for (int k = b; k < e; ++k) tasks += tasks_of(P->jobs[k], n_nodes);
+    if (tasks > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many wave tasks");
+    a.jobs = P->d_jobs + b;
+    a.task_start = ws.task_start + b;
+    a.n_jobs = e - b;
+    a.total_tasks = int(tasks);
+    CGTP_HIP(launch_conv(a, c, s));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,11 @@
+// One kernel class of the fused CGTP convolution (the class is chosen at build time
+// with -DCGTP_CONV_CLASS=<k>; the build compiles this file once per class).
+#include "conv_kernel.hpp"
+
+#ifndef CGTP_CONV_CLASS
+#error "CGTP_CONV_CLASS must be defined"
+#endif
+
+namespace cgtp {
+template hipError_t launch_conv_class<CGTP_CONV_CLASS>(const ConvArgs& args, hipStream_t s);
+}  // namespace cgtp

@@ -1,0 +1,563 @@
+// Graph-side kernels: receiver-CSR neighbour list, mask prepare (active CSR and node
+// order) and the per-edge pass that compacts active edges and evaluates the edge
+// harmonics.  All integer outputs are deterministic: atomics are used only for
+// counts, and every order-dependent result is sorted or scanned afterwards.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "launch.hpp"
+#include "sh_eval.hpp"
+#include "variants.hpp"
+
+namespace cgtp {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / kWave;
+
+__device__ inline int lane_id() { return __lane_id(); }
+
+// Block-wide exclusive scan of one value per thread (1024 threads).  `wsum` holds
+// kScanWaves ints of LDS.  Returns the exclusive prefix and sets `total`.
+__device__ inline int block_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int t = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += t;
+  }
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int k = 0; k < kScanWaves; ++k) {
+      int t = wsum[k];
+      wsum[k] = run;
+      run += t;
+    }
+    wsum[kScanWaves] = run;
+  }
+  __syncthreads();
+  int excl = wsum[wave] + inc - v;
+  total = wsum[kScanWaves];
+  __syncthreads();
+  return excl;
+}
+
+// out[k] = sum_{q<k} in[q] for k <= n (out has n+1 entries).  One workgroup.
+__global__ void __launch_bounds__(kScanThreads) scan_exclusive_kernel(const int32_t* in, int32_t* out, int n) {
+  __shared__ int wsum[kScanWaves + 1];
+  int carry = 0;
+  for (int base = 0; base < n; base += kScanThreads) {
+    const int idx = base + threadIdx.x;
+    const int v = idx < n ? in[idx] : 0;
+    int total;
+    const int ex = block_exclusive_scan(v, wsum, total);
+    if (idx < n) out[idx] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+}
+
+// ---------------------------------------------------------------------------------
+// Neighbour list.  Predicate in fp64 with contraction disabled, so that the result is
+// the same bit for bit as any implementation that follows the stated operation order.
+// ---------------------------------------------------------------------------------
+
+struct GridArgs {
+  int nc[3];
+  double box[3];
+  double rc2;
+};
+
+__device__ inline bool pair_within(const float* __restrict__ pos, int i, int j, const GridArgs& g,
+                                   int8_t* s) {
+#pragma clang fp contract(off)
+  double d[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    double dk = double(pos[3 * j + k]) - double(pos[3 * i + k]);
+    const double half = 0.5 * g.box[k];
+    int8_t sk = 0;
+    if (dk > half) {
+      dk = dk - g.box[k];
+      sk = -1;
+    } else if (dk < -half) {
+      dk = dk + g.box[k];
+      sk = 1;
+    }
+    d[k] = dk;
+    s[k] = sk;
+  }
+  const double r2 = (d[0] * d[0] + d[1] * d[1]) + d[2] * d[2];
+  return r2 < g.rc2;
+}
+
+__device__ inline int cell_coord(float x, double box, int nc) {
+  int c = int(floor(double(x) * double(nc) / box));
+  return c < 0 ? 0 : (c >= nc ? nc - 1 : c);
+}
+
+__global__ void fill_i32_kernel(int32_t* __restrict__ p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void nbr_assign_kernel(const float* __restrict__ pos, int n, GridArgs g,
+                                  int32_t* __restrict__ atom_cell, int32_t* __restrict__ cell_count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int cx = cell_coord(pos[3 * i + 0], g.box[0], g.nc[0]);
+  const int cy = cell_coord(pos[3 * i + 1], g.box[1], g.nc[1]);
+  const int cz = cell_coord(pos[3 * i + 2], g.box[2], g.nc[2]);
+  const int c = (cz * g.nc[1] + cy) * g.nc[0] + cx;
+  atom_cell[i] = c;
+  atomicAdd(&cell_count[c], 1);
+}
+
+__global__ void nbr_bin_kernel(int n, const int32_t* __restrict__ atom_cell,
+                               const int32_t* __restrict__ cell_start, int32_t* __restrict__ cursor,
+                               int32_t* __restrict__ cell_atoms) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int c = atom_cell[i];
+  cell_atoms[cell_start[c] + atomicAdd(&cursor[c], 1)] = i;
+}
+
+// Visit every distinct stencil cell once (a dimension with 1 or 2 cells would
+// otherwise be visited twice through the periodic wrap).
+template <typename F>
+__device__ inline void for_each_stencil_cell(int c, const GridArgs& g, F&& f) {
+  const int cx = c % g.nc[0];
+  const int cy = (c / g.nc[0]) % g.nc[1];
+  const int cz = c / (g.nc[0] * g.nc[1]);
+  const int lo[3] = {g.nc[0] >= 3 ? -1 : 0, g.nc[1] >= 3 ? -1 : 0, g.nc[2] >= 3 ? -1 : 0};
+  const int hi[3] = {g.nc[0] >= 2 ? 1 : 0, g.nc[1] >= 2 ? 1 : 0, g.nc[2] >= 2 ? 1 : 0};
+  for (int dz = lo[2]; dz <= hi[2]; ++dz) {
+    const int z = (cz + dz + g.nc[2]) % g.nc[2];
+    for (int dy = lo[1]; dy <= hi[1]; ++dy) {
+      const int y = (cy + dy + g.nc[1]) % g.nc[1];
+      for (int dx = lo[0]; dx <= hi[0]; ++dx) {
+        const int x = (cx + dx + g.nc[0]) % g.nc[0];
+        f((z * g.nc[1] + y) * g.nc[0] + x);
+      }
+    }
+  }
+}
+
+__global__ void nbr_count_kernel(const float* __restrict__ pos, int n, GridArgs g,
+                                 const int32_t* __restrict__ atom_cell,
+                                 const int32_t* __restrict__ cell_start,
+                                 const int32_t* __restrict__ cell_atoms, int32_t* __restrict__ row_count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int cnt = 0;
+  for_each_stencil_cell(atom_cell[i], g, [&](int c) {
+    for (int k = cell_start[c]; k < cell_start[c + 1]; ++k) {
+      const int j = cell_atoms[k];
+      int8_t s[3];
+      if (j != i && pair_within(pos, i, j, g, s)) ++cnt;
+    }
+  });
+  row_count[i] = cnt;
+}
+
+__global__ void nbr_fill_kernel(const float* __restrict__ pos, int n, GridArgs g,
+                                const int32_t* __restrict__ atom_cell,
+                                const int32_t* __restrict__ cell_start,
+                                const int32_t* __restrict__ cell_atoms,
+                                const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col,
+                                int8_t* __restrict__ shift) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int beg = row_ptr[i];
+  int end = beg;
+  for_each_stencil_cell(atom_cell[i], g, [&](int c) {
+    for (int k = cell_start[c]; k < cell_start[c + 1]; ++k) {
+      const int j = cell_atoms[k];
+      int8_t s[3];
+      if (j != i && pair_within(pos, i, j, g, s)) {
+        col[end] = j;
+        shift[3 * end + 0] = s[0];
+        shift[3 * end + 1] = s[1];
+        shift[3 * end + 2] = s[2];
+        ++end;
+      }
+    }
+  });
+  // rows are short: insertion sort by j (j values within a row are distinct)
+  for (int a = beg + 1; a < end; ++a) {
+    const int key = col[a];
+    const int8_t s0 = shift[3 * a], s1 = shift[3 * a + 1], s2 = shift[3 * a + 2];
+    int b = a - 1;
+    while (b >= beg && col[b] > key) {
+      col[b + 1] = col[b];
+      shift[3 * (b + 1) + 0] = shift[3 * b + 0];
+      shift[3 * (b + 1) + 1] = shift[3 * b + 1];
+      shift[3 * (b + 1) + 2] = shift[3 * b + 2];
+      --b;
+    }
+    col[b + 1] = key;
+    shift[3 * (b + 1) + 0] = s0;
+    shift[3 * (b + 1) + 1] = s1;
+    shift[3 * (b + 1) + 2] = s2;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Mask prepare.
+// ---------------------------------------------------------------------------------
+
+__global__ void prep_count_kernel(const int32_t* __restrict__ row_ptr, const uint8_t* __restrict__ mask,
+                                  int n, int32_t* __restrict__ deg) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int beg = row_ptr[i], end = row_ptr[i + 1];
+  int d = end - beg;
+  if (mask) {
+    d = 0;
+    for (int e = beg; e < end; ++e) d += (mask[e] != 0);
+  }
+  deg[i] = d;
+}
+
+// One workgroup: act_row_ptr = exclusive scan of deg; order = node ids sorted by deg
+// descending, ties by id ascending (stable LSD radix sort on maxdeg - deg, 8-bit
+// digits, ranks inside a wave from ballots, across waves from an LDS table).
+__global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int32_t* __restrict__ deg, int n,
+                                                                      int32_t* __restrict__ act_row_ptr,
+                                                                      int32_t* __restrict__ order,
+                                                                      int32_t* __restrict__ tmp_a,
+                                                                      int32_t* __restrict__ tmp_b) {
+  __shared__ int wsum[kScanWaves + 1];
+  __shared__ int s_max;
+  __shared__ int hist[256];
+  __shared__ int base[256];
+  __shared__ int tile_tot[256];
+  __shared__ int wcnt[kScanWaves][256];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+
+  // 1. scan and maximum
+  if (tid == 0) s_max = 0;
+  __syncthreads();
+  int carry = 0;
+  int local_max = 0;
+  for (int b0 = 0; b0 < n; b0 += kScanThreads) {
+    const int idx = b0 + tid;
+    const int v = idx < n ? deg[idx] : 0;
+    local_max = v > local_max ? v : local_max;
+    int total;
+    const int ex = block_exclusive_scan(v, wsum, total);
+    if (idx < n) act_row_ptr[idx] = carry + ex;
+    carry += total;
+  }
+  if (tid == 0) act_row_ptr[n] = carry;
+  atomicMax(&s_max, local_max);
+  __syncthreads();
+  const int maxdeg = s_max;
+
+  int passes = 0;
+  for (int m = maxdeg; m > 0; m >>= 8) ++passes;
+  if (passes == 0) {
+    for (int idx = tid; idx < n; idx += kScanThreads) order[idx] = idx;
+    return;
+  }
+
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  for (int p = 0; p < passes; ++p) {
+    const int32_t* src = (p == 0) ? nullptr : ((p - 1) % 2 == 0 ? tmp_a : tmp_b);
+    int32_t* dst = (p == passes - 1) ? order : (p % 2 == 0 ? tmp_a : tmp_b);
+    const int shift = 8 * p;
+    for (int k = tid; k < 256; k += kScanThreads) hist[k] = 0;
+    __syncthreads();
+    for (int idx = tid; idx < n; idx += kScanThreads) {
+      const int id = src ? src[idx] : idx;
+      const int digit = ((maxdeg - deg[id]) >> shift) & 255;
+      atomicAdd(&hist[digit], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int k = 0; k < 256; ++k) {
+        base[k] = run;
+        run += hist[k];
+      }
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < n; b0 += kScanThreads) {
+      const int idx = b0 + tid;
+      const bool valid = idx < n;
+      const int id = valid ? (src ? src[idx] : idx) : 0;
+      const int digit = valid ? (((maxdeg - deg[id]) >> shift) & 255) : 0;
+      unsigned long long same = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (digit >> bit) & 1;
+        const unsigned long long bb = __ballot(on);
+        same &= on ? bb : ~bb;
+      }
+      const int rank = __popcll(same & lt_mask);
+      const int cnt = __popcll(same);
+      for (int k = tid; k < kScanWaves * 256; k += kScanThreads) (&wcnt[0][0])[k] = 0;
+      __syncthreads();
+      if (valid && rank == 0) wcnt[wave][digit] = cnt;
+      __syncthreads();
+      if (tid < 256) {
+        int run = 0;
+        for (int w = 0; w < kScanWaves; ++w) {
+          const int t = wcnt[w][tid];
+          wcnt[w][tid] = run;
+          run += t;
+        }
+        tile_tot[tid] = run;
+      }
+      __syncthreads();
+      if (valid) dst[base[digit] + wcnt[wave][digit] + rank] = id;
+      __syncthreads();
+      if (tid < 256) base[tid] += tile_tot[tid];
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Per-edge pass: receiver by binary search over row_ptr; position among the active
+// edges of the row; compacted ids; edge vector and harmonics in fp64.
+// ---------------------------------------------------------------------------------
+
+struct EdgeArgs {
+  const float* pos;
+  const int32_t* row_ptr;
+  const int32_t* col;
+  const int8_t* shift;
+  const uint8_t* mask;
+  const int32_t* act_row_ptr;
+  int32_t* act_eid;
+  int32_t* act_col;
+  float* sh;
+  int n_nodes;
+  int n_edges;
+  int has_cell;
+  int sh_stride;
+  double cell[9];
+};
+
+template <int L>
+__global__ void edge_pass_kernel(EdgeArgs a) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.n_edges) return;
+  if (a.mask && a.mask[e] == 0) return;
+  int lo = 0, hi = a.n_nodes;  // find i with row_ptr[i] <= e < row_ptr[i+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.row_ptr[mid] <= e) lo = mid; else hi = mid;
+  }
+  const int i = lo;
+  const int rbeg = a.row_ptr[i];
+  int pos_in_row = e - rbeg;
+  if (a.mask) {
+    pos_in_row = 0;
+    for (int q = rbeg; q < e; ++q) pos_in_row += (a.mask[q] != 0);
+  }
+  const int slot = a.act_row_ptr[i] + pos_in_row;
+  if (a.act_eid) a.act_eid[slot] = e;
+  if (!a.act_col && !a.sh) return;  // col (and pos) are only needed by these outputs
+  const int j = a.col[e];
+  if (a.act_col) a.act_col[slot] = j;
+  if (!a.sh) return;
+
+  double r[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) r[k] = double(a.pos[3 * j + k]) - double(a.pos[3 * i + k]);
+  if (a.has_cell && a.shift) {
+    const double s0 = a.shift[3 * e + 0], s1 = a.shift[3 * e + 1], s2 = a.shift[3 * e + 2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) r[k] = r[k] + s0 * a.cell[k] + s1 * a.cell[3 + k] + s2 * a.cell[6 + k];
+  }
+  const double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  constexpr int NY = (L + 1) * (L + 1);
+  double Y[NY];
+  if (rr > 0.0) {
+    const double inv = 1.0 / rr;
+    sh_unit<L>(r[0] * inv, r[1] * inv, r[2] * inv, Y);
+  } else {
+#pragma unroll
+    for (int q = 0; q < NY; ++q) Y[q] = 0.0;
+    Y[0] = 1.0;
+  }
+  float* out = a.sh + (long)slot * a.sh_stride;
+#pragma unroll
+  for (int q = 0; q < NY; ++q) out[q] = float(Y[q]);
+}
+
+__global__ void task_prefix_kernel(const Job* __restrict__ jobs, int n_jobs, int n_nodes,
+                                   int32_t* __restrict__ task_start) {
+  if (threadIdx.x != 0) return;
+  int run = 0;
+  for (int k = 0; k < n_jobs; ++k) {
+    task_start[k] = run;
+    const int s = 64 >> jobs[k].lanes_log2;
+    run += (n_nodes + s - 1) / s;
+  }
+  task_start[n_jobs] = run;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------------
+
+NbrGrid make_nbr_grid(int64_t n, const float box[3], float cutoff) {
+  NbrGrid g{};
+  const double rc = double(cutoff);
+  g.rc2 = rc * rc;
+  // cells no smaller than the cutoff (with a margin for rounding in the binning),
+  // and no more cells than about 2 per atom
+  const double cap = std::max(1.0, std::cbrt(2.0 * double(std::max<int64_t>(n, 1))) + 1.0);
+  for (int k = 0; k < 3; ++k) {
+    g.box[k] = double(box[k]);
+    int nc = int(std::floor(g.box[k] / (rc * (1.0 + 1e-6))));
+    nc = std::max(1, std::min(nc, int(cap)));
+    g.nc[k] = nc;
+  }
+  return g;
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+size_t nbr_workspace_bytes(int64_t n, const NbrGrid& g) {
+  const size_t nc = size_t(g.n_cells());
+  return align256(nc * 4) + align256((nc + 1) * 4) + 3 * align256(size_t(n) * 4 + 4);
+}
+
+NbrWorkspace carve_nbr_workspace(void* ws, int64_t n, const NbrGrid& g) {
+  char* p = static_cast<char*>(ws);
+  const size_t nc = size_t(g.n_cells());
+  NbrWorkspace w{};
+  w.cell_count = reinterpret_cast<int32_t*>(p);
+  p += align256(nc * 4);
+  w.cell_start = reinterpret_cast<int32_t*>(p);
+  p += align256((nc + 1) * 4);
+  w.atom_cell = reinterpret_cast<int32_t*>(p);
+  p += align256(size_t(n) * 4 + 4);
+  w.cell_atoms = reinterpret_cast<int32_t*>(p);
+  p += align256(size_t(n) * 4 + 4);
+  w.row_count = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+static GridArgs to_args(const NbrGrid& g) {
+  GridArgs a{};
+  for (int k = 0; k < 3; ++k) {
+    a.nc[k] = g.nc[k];
+    a.box[k] = g.box[k];
+  }
+  a.rc2 = g.rc2;
+  return a;
+}
+
+hipError_t launch_nbr_count(const float* pos, int n, const NbrGrid& g, const NbrWorkspace& w,
+                            int32_t* row_ptr, hipStream_t s) {
+  const GridArgs a = to_args(g);
+  const int nc = g.n_cells();
+  const int tb = 256;
+  // cell_count doubles as the fill cursor: clear, count, scan, clear, bin
+  fill_i32_kernel<<<ceil_div(nc, tb), tb, 0, s>>>(w.cell_count, nc, 0);
+  if (n > 0) nbr_assign_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_count);
+  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.cell_count, w.cell_start, nc);
+  fill_i32_kernel<<<ceil_div(nc, tb), tb, 0, s>>>(w.cell_count, nc, 0);
+  if (n > 0) {
+    nbr_bin_kernel<<<ceil_div(n, tb), tb, 0, s>>>(n, w.atom_cell, w.cell_start, w.cell_count, w.cell_atoms);
+    nbr_count_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start, w.cell_atoms,
+                                                    w.row_count);
+  }
+  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.row_count, row_ptr, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrWorkspace& w,
+                           const int32_t* row_ptr, int32_t* col, int8_t* shift, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const GridArgs a = to_args(g);
+  const int tb = 256;
+  nbr_fill_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start, w.cell_atoms, row_ptr,
+                                                 col, shift);
+  return hipGetLastError();
+}
+
+hipError_t launch_prepare_rows(const int32_t* row_ptr, const uint8_t* mask, int n, int32_t* deg,
+                               int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a, int32_t* tmp_b,
+                               hipStream_t s) {
+  const int tb = 256;
+  if (n > 0) prep_count_kernel<<<ceil_div(n, tb), tb, 0, s>>>(row_ptr, mask, n, deg);
+  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, act_row_ptr, order, tmp_a, tmp_b);
+  return hipGetLastError();
+}
+
+hipError_t launch_edge_pass(const EdgeGeom& g, int32_t* act_eid, int32_t* act_col, float* sh, int l_sh_max,
+                            hipStream_t s) {
+  if (g.n_edges == 0 || g.n_nodes == 0) return hipSuccess;
+  if (!g.row_ptr || !g.act_row_ptr) return hipErrorInvalidValue;
+  if ((act_col || sh) && !g.col) return hipErrorInvalidValue;
+  if (sh && !g.pos) return hipErrorInvalidValue;
+  EdgeArgs a{};
+  a.pos = g.pos;
+  a.row_ptr = g.row_ptr;
+  a.col = g.col;
+  a.shift = g.shift;
+  a.mask = g.mask;
+  a.act_row_ptr = g.act_row_ptr;
+  a.act_eid = act_eid;
+  a.act_col = act_col;
+  a.sh = sh;
+  a.n_nodes = g.n_nodes;
+  a.n_edges = g.n_edges;
+  a.has_cell = g.has_cell;
+  a.sh_stride = (l_sh_max + 1) * (l_sh_max + 1);
+  for (int k = 0; k < 9; ++k) a.cell[k] = g.cell[k];
+  const int tb = 256;
+  const int nb = ceil_div(g.n_edges, tb);
+  switch (l_sh_max) {
+    case 0: edge_pass_kernel<0><<<nb, tb, 0, s>>>(a); break;
+    case 1: edge_pass_kernel<1><<<nb, tb, 0, s>>>(a); break;
+    case 2: edge_pass_kernel<2><<<nb, tb, 0, s>>>(a); break;
+    case 3: edge_pass_kernel<3><<<nb, tb, 0, s>>>(a); break;
+    case 4: edge_pass_kernel<4><<<nb, tb, 0, s>>>(a); break;
+    case 5: edge_pass_kernel<5><<<nb, tb, 0, s>>>(a); break;
+    case 6: edge_pass_kernel<6><<<nb, tb, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_task_prefix(const Job* jobs, int n_jobs, int n_nodes, int32_t* task_start, hipStream_t s) {
+  task_prefix_kernel<<<1, 64, 0, s>>>(jobs, n_jobs, n_nodes, task_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& args, int variant_class, hipStream_t s) {
+  switch (variant_class) {
+    case 0: return launch_conv_class<0>(args, s);
+    case 1: return launch_conv_class<1>(args, s);
+    case 2: return launch_conv_class<2>(args, s);
+    case 3: return launch_conv_class<3>(args, s);
+    case 4: return launch_conv_class<4>(args, s);
+    case 5: return launch_conv_class<5>(args, s);
+    case 6: return launch_conv_class<6>(args, s);
+    case 7: return launch_conv_class<7>(args, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static_assert(kNumClasses == 8, "launch_conv covers every kernel class");
+
+}  // namespace cgtp

@@ -1,0 +1,271 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: neighbour list and mask prepare bit-exact; edge harmonics within 2e-6 absolute
+(fp64 evaluation stored as fp32); convolution relative L2 <= 1e-5 and max |diff| <= 1e-4
+over the whole output, plus bitwise run-to-run determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as WL
+
+C = pytest.importorskip("clebsch_gordan_tensor_node_amd")
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-5
+MAX_ABS = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a device"
+    return torch.device("cuda:0")
+
+
+def _t(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+_CACHE = {}
+
+
+def _workload(name):
+    """Inputs drawn once per workload (oracle neighbour list fixes E for the draws)."""
+    if name in _CACHE:
+        return _CACHE[name]
+    wl = WL.WORKLOADS[name]
+    pos, box, cell, rng = WL.positions(wl)
+    rp, col, sh = O.neighbors(pos, box, wl.cutoff)
+    plan = O.build_plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    x, w, mask = WL.draw_payload(wl, rng, wl.n_atoms, plan.f_in, len(col), plan.w_per_edge)
+    _CACHE[name] = (wl, plan, pos, box, cell, rp, col, sh, x, w, mask)
+    return _CACHE[name]
+
+
+def _compare(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, what
+    assert np.all(np.isfinite(got)), what
+    diff = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(diff) / nref if nref > 0 else np.linalg.norm(diff)
+    mx = np.abs(diff).max() if diff.size else 0.0
+    print(f"{what}: rel_l2={rel:.3e} max_abs={mx:.3e}", flush=True)
+    assert rel <= REL_L2 and mx <= MAX_ABS, (what, rel, mx)
+
+
+# ----------------------------------------------------------------------------------
+# neighbour list
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", WL.ORDER)
+def test_neighbors_bit_exact(dev, name):
+    wl, plan, pos, box, cell, rp, col, sh, *_ = _workload(name)
+    g_rp, g_col, g_sh = C.neighbors_build(_t(pos, dev), box, wl.cutoff)
+    assert np.array_equal(g_rp.cpu().numpy(), rp)
+    assert np.array_equal(g_col.cpu().numpy(), col)
+    assert np.array_equal(g_sh.cpu().numpy(), sh)
+
+
+@pytest.mark.parametrize("n,box_len,cutoff,seed", [
+    (1, 5.0, 2.0, 0), (2, 3.0, 1.4, 1), (20, 3.0, 1.4, 2), (50, 4.5, 1.5, 3), (300, 9.0, 2.9, 4),
+    (700, 20.0, 1.0, 5)])
+def test_neighbors_small_boxes(dev, n, box_len, cutoff, seed):
+    # 1, 2 and 3 cells per side (the stencil wraps onto itself), and sparse cases
+    rng = np.random.default_rng(seed)
+    pos = (rng.random((n, 3)) * box_len).astype(np.float32)
+    pos[pos >= np.float32(box_len)] = 0
+    box = np.full(3, box_len, dtype=np.float32)
+    rp, col, sh = O.neighbors(pos, box, cutoff)
+    g_rp, g_col, g_sh = C.neighbors_build(_t(pos, dev), box, cutoff, edge_capacity=3)  # forces the retry
+    assert np.array_equal(g_rp.cpu().numpy(), rp)
+    assert np.array_equal(g_col.cpu().numpy(), col)
+    assert np.array_equal(g_sh.cpu().numpy(), sh)
+
+
+def test_neighbors_empty(dev):
+    pos = torch.zeros((0, 3), dtype=torch.float32, device=dev)
+    rp, col, sh = C.neighbors_build(pos, [5.0, 5.0, 5.0], 2.0)
+    assert rp.cpu().tolist() == [0] and col.numel() == 0
+
+
+# ----------------------------------------------------------------------------------
+# mask prepare
+# ----------------------------------------------------------------------------------
+
+def _check_prepare(dev, rp, mask, n_edges):
+    plan = C.Plan("4x0e", "1x0e", 0, "all")
+    a, e, o = C.conv_prepare(plan, _t(rp, dev), None if mask is None else _t(mask, dev), n_edges)
+    ra, re_, ro = O.prepare(rp, mask)
+    a = a.cpu().numpy()
+    assert np.array_equal(a, ra)
+    assert np.array_equal(e.cpu().numpy()[:a[-1]], re_)
+    assert np.array_equal(o.cpu().numpy(), ro)
+
+
+@pytest.mark.parametrize("name", ["c1_768", "si_mask"])
+def test_prepare_workloads(dev, name):
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload(name)
+    _check_prepare(dev, rp, mask, len(col))
+
+
+@pytest.mark.parametrize("seed,n,maxdeg,masked", [(0, 1, 3, True), (1, 37, 0, False), (2, 1500, 40, True),
+                                                  (3, 5000, 300, True), (4, 3000, 70000, False)])
+def test_prepare_random(dev, seed, n, maxdeg, masked):
+    # maxdeg 300 and 70000 need two and three radix passes; empty rows included
+    rng = np.random.default_rng(seed)
+    deg = rng.integers(0, maxdeg + 1, n)
+    if maxdeg > 1000:
+        deg = np.where(rng.random(n) < 0.002, deg, deg % 50)
+    rp = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
+    e = int(rp[-1])
+    mask = (rng.random(e) < 0.5).astype(np.uint8) if masked else None
+    _check_prepare(dev, rp, mask, e)
+
+
+# ----------------------------------------------------------------------------------
+# edge harmonics
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "highl_768", "si_mask"])
+def test_edge_sh(dev, name):
+    wl, plan, pos, box, cell, rp, col, sh, *_ = _workload(name)
+    p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    got = C.edge_sh(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev)).cpu().numpy()
+    r = O.edge_vectors(pos, cell, rp, col, sh)
+    ref = np.concatenate([O.real_sh(l, r) for l in range(plan.l_sh_max + 1)], 1)
+    assert np.abs(got - ref).max() <= 2e-6
+
+
+# ----------------------------------------------------------------------------------
+# convolution
+# ----------------------------------------------------------------------------------
+
+def _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask, plan=None):
+    p = plan or C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    out = C.conv_forward(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev), _t(x, dev),
+                         _t(w, dev), None if mask is None else _t(mask, dev))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "c1_768", "c2_768", "si_mask"])
+def test_conv_full_workloads(dev, name):
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload(name)
+    got = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
+    ref = O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask)
+    _compare(got, ref, name)
+
+
+def _sub_csr(rp, rows):
+    segs = [np.arange(rp[i], rp[i + 1]) for i in rows]
+    eids = np.concatenate(segs) if segs else np.zeros(0, np.int64)
+    srp = np.concatenate([[0], np.cumsum([len(s) for s in segs])])
+    return srp, eids
+
+
+def test_conv_high_l_sampled(dev):
+    # full-size launch on the GPU; the oracle evaluates a sample of 48 receivers
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("highl_768")
+    got = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
+    rows = np.random.default_rng(0).choice(wl.n_atoms, 48, replace=False)
+    srp, eids = _sub_csr(rp, rows)
+    # receivers become 0..47 of a sub-graph whose senders keep their original ids
+    n = wl.n_atoms
+    pos_sub = np.concatenate([pos[rows], pos])
+    col_sub = (col[eids] + len(rows)).astype(np.int32)
+    x_sub = np.concatenate([x[rows], x])
+    rp_full = np.concatenate([srp, np.full(n, srp[-1])]).astype(np.int32)
+    ref = O.conv_forward(plan, pos_sub, cell, rp_full, col_sub, sh[eids], x_sub, w[eids], None)[:len(rows)]
+    _compare(got[rows], ref, "highl_768[48 rows]")
+
+
+def _small_system(n, box_len, cutoff, seed):
+    rng = np.random.default_rng(seed)
+    pos = (rng.random((n, 3)) * box_len).astype(np.float32)
+    pos[pos >= np.float32(box_len)] = 0
+    box = np.full(3, box_len, dtype=np.float32)
+    cell = np.diag(box).astype(np.float32)
+    rp, col, sh = O.neighbors(pos, box, cutoff)
+    return rng, pos, box, cell, rp, col, sh
+
+
+@pytest.mark.parametrize("l1", range(7))
+@pytest.mark.parametrize("mul", [4, 3, 72])
+def test_conv_every_variant(dev, l1, mul):
+    """Every (l1, l2, l3) specialisation, K = 4 (mul 4, 72: two channel blocks at l1 <= 1
+    when 72 > 64) and K = 1 (mul 3), against the oracle on a small periodic system."""
+    rng, pos, box, cell, rp, col, sh = _small_system(40, 6.0, 2.6, 100 + l1)
+    for l2 in range(7):
+        spec_in, spec_sh = f"{mul}x{l1}e", f"1x{l2}e"
+        plan = O.build_plan(spec_in, spec_sh, 6, O.PATHS_ALL)
+        x = rng.standard_normal((len(pos), plan.f_in)).astype(np.float32)
+        w = rng.standard_normal((len(col), plan.w_per_edge)).astype(np.float32)
+        p = C.Plan(spec_in, spec_sh, 6, "all")
+        got = C.conv_forward(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev), _t(x, dev),
+                             _t(w, dev)).cpu().numpy()
+        ref = O.conv_forward(plan, pos, cell, rp, col, sh, x, w)
+        _compare(got, ref, f"{spec_in} x {spec_sh}")
+
+
+def test_conv_large_multiplicity_blocks(dev):
+    # 300 channels: K = 4, two full blocks of 256 lanes*K and a ragged one
+    rng, pos, box, cell, rp, col, sh = _small_system(30, 5.0, 2.4, 7)
+    spec_in, spec_sh = "300x1o+520x0e", "1x0e+1x1o"
+    plan = O.build_plan(spec_in, spec_sh, 1, O.PATHS_PARITY)
+    x = rng.standard_normal((len(pos), plan.f_in)).astype(np.float32)
+    w = rng.standard_normal((len(col), plan.w_per_edge)).astype(np.float32)
+    p = C.Plan(spec_in, spec_sh, 1, "parity")
+    got = C.conv_forward(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev), _t(x, dev),
+                         _t(w, dev)).cpu().numpy()
+    _compare(got, O.conv_forward(plan, pos, cell, rp, col, sh, x, w), "large mul")
+
+
+def test_conv_deterministic_and_nan_safe(dev):
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("si_mask")
+    a = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
+    b = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
+    assert np.array_equal(a, b)                 # bitwise run to run
+    wn = w.copy()
+    wn[mask == 0] = np.nan                      # inactive edges are never read
+    c = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, wn, mask)
+    assert np.array_equal(a, c)
+    z = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, np.zeros_like(mask))
+    assert np.all(z == 0.0)
+
+
+def test_conv_empty_graphs(dev):
+    p = C.Plan("8x0e+8x1o", "1x0e+1x1o", 1, "all")
+    pos = np.array([[0.5, 0.5, 0.5], [4.0, 4.0, 4.0]], dtype=np.float32)
+    rp = np.zeros(3, dtype=np.int32)
+    x = np.ones((2, 32), dtype=np.float32)
+    out = C.conv_forward(p, _t(pos, dev), np.eye(3, dtype=np.float32) * 9, _t(rp, dev),
+                         torch.zeros(0, dtype=torch.int32, device=dev), torch.zeros((0, 3), dtype=torch.int8, device=dev),
+                         _t(x, dev), torch.zeros((0, 40), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item()
+
+
+def test_conv_equivariance_fp32(dev):
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("c2_768")
+    ref = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
+    rng = np.random.default_rng(3)
+    R = O.random_rotation(rng)
+
+    def rot(irreps, y):
+        y = np.array(y, dtype=np.float64)
+        off = 0
+        for mul, l, _ in irreps:
+            n = 2 * l + 1
+            D = O.wigner_d_real(l, R)
+            y[:, off:off + mul * n] = (y[:, off:off + mul * n].reshape(-1, mul, n) @ D.T).reshape(-1, mul * n)
+            off += mul * n
+        return y
+
+    pos_r = (pos.astype(np.float64) @ R.T).astype(np.float32)
+    cell_r = (cell.astype(np.float64) @ R.T).astype(np.float32)
+    got = _gpu_conv(dev, wl, pos_r, cell_r, rp, col, sh, rot(plan.irreps_in, x).astype(np.float32), w, mask)
+    _compare(got, rot(plan.irreps_out, ref), "c2_768 rotated")
