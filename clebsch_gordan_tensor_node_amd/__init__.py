@@ -199,8 +199,13 @@ def edge_sh(plan: Plan, pos, cell, row_ptr, col, shift):
     return sh[:e]
 
 
-def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, out=None, workspace=None):
-    """out[N, f_out] of the CGTP convolution (asynchronous on the current stream)."""
+def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, out=None, workspace=None,
+                 conv_events=None):
+    """out[N, f_out] of the CGTP convolution (asynchronous on the current stream).
+
+    conv_events: optional (begin, end) torch.cuda.Event pair (each recorded once before,
+    so that its HIP event exists); the library records them around the fused
+    convolution kernel launches."""
     lib = load()
     _dev(pos, torch.float32, "pos")
     n = pos.shape[0]
@@ -218,8 +223,12 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, ou
     _dev(out, torch.float32, "out", (n, plan.f_out))
     ws = _workspace(plan.workspace_size(n, e, mask is not None), pos.device, workspace)
     cella = _host_f32(cell, 9, "cell")
-    check(lib.cgtp_conv_forward(plan.handle, _ptr(pos), n,
-                                None if cella is None else cella.ctypes.data_as(_lib.FP),
-                                _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask),
-                                _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    args = (plan.handle, _ptr(pos), n, None if cella is None else cella.ctypes.data_as(_lib.FP),
+            _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask),
+            _ptr(out), _ptr(ws), ws.numel(), _stream())
+    if conv_events is None:
+        check(lib.cgtp_conv_forward(*args))
+    else:
+        b, t = conv_events
+        check(lib.cgtp_conv_forward_timed(*args, ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(t.cuda_event)))
     return out

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcgtp.so")
-N_CONV_CLASSES = 8
+N_CONV_CLASSES = 9
 
 ARCH = "gfx950"
 FLAGS = [

@@ -143,12 +143,15 @@ struct cgtp_plan_s {
   int l_sh_max = 0;
   int sh_stride = 1;
   std::string irreps_out;
-  std::vector<Job> jobs;             // grouped by kernel class, heavy jobs first
-  std::vector<int> class_begin;      // [kNumClasses + 1]
+  std::vector<Job> jobs;             // ordered by group
+  std::vector<Group> groups;         // by kernel class, heavy groups first
+  std::vector<int> class_begin;      // [kNumClasses + 1] first group of each class
   int n_variants = 0;
   bool host_only = true;
   int device = -1;
+  void* d_tables = nullptr;          // device copy: jobs, then groups
   Job* d_jobs = nullptr;
+  Group* d_groups = nullptr;
 };
 
 namespace {
@@ -166,8 +169,11 @@ void schedule(cgtp_plan_s& P) {
     double cost;
   };
   std::vector<Tmp> tmp;
+  std::vector<int> tmp_irrep, tmp_block;
   std::vector<int> used(kNumVariants, 0);
   const bool strides4 = (P.f_in % 4 == 0) && (P.f_out % 4 == 0) && (P.w % 4 == 0);
+  int plan_lmax = 0;
+  for (const PathInfo& p : P.paths) plan_lmax = std::max(plan_lmax, std::max(p.l1, std::max(p.l2, p.l3)));
   for (size_t pi = 0; pi < P.paths.size(); ++pi) {
     const PathInfo& p = P.paths[pi];
     const bool al = strides4 && p.mul % 4 == 0 && p.in_off % 4 == 0 && p.out_off % 4 == 0 && p.w_off % 4 == 0;
@@ -192,6 +198,7 @@ void schedule(cgtp_plan_s& P) {
     const int block = 64 * K;
     for (int c0 = 0; c0 < p.mul; c0 += block) {
       const int n_ch = std::min(block, p.mul - c0);
+      // lanes per receiver; the remaining lane bits select the receiver of the wave
       const int lanes = next_pow2((n_ch + K - 1) / K);
       Job j{};
       j.variant = v;
@@ -202,32 +209,86 @@ void schedule(cgtp_plan_s& P) {
       j.w_off = p.w_off + c0;
       j.sh_off = p.l2 * p.l2;
       j.path = int(pi);
-      tmp.push_back(Tmp{j, variant_class(v), cost});
+      tmp.push_back(Tmp{j, job_class(v, plan_lmax), cost});
+      tmp_irrep.push_back(p.i_in);
+      tmp_block.push_back(c0);
     }
   }
-  std::stable_sort(tmp.begin(), tmp.end(), [](const Tmp& a, const Tmp& b) {
-    if (a.cls != b.cls) return a.cls < b.cls;
-    return a.cost > b.cost;
+  // groups: (class, input irrep, channel block); heavy groups first inside a class,
+  // heavy jobs first inside a group
+  struct Key {
+    int cls, irrep, block;
+    bool operator<(const Key& o) const {
+      if (cls != o.cls) return cls < o.cls;
+      if (irrep != o.irrep) return irrep < o.irrep;
+      return block < o.block;
+    }
+    bool operator==(const Key& o) const { return cls == o.cls && irrep == o.irrep && block == o.block; }
+  };
+  std::vector<Key> keys;
+  for (size_t k = 0; k < tmp.size(); ++k) keys.push_back(Key{tmp[k].cls, tmp_irrep[k], tmp_block[k]});
+  std::vector<Key> uniq = keys;
+  std::sort(uniq.begin(), uniq.end());
+  uniq.erase(std::unique(uniq.begin(), uniq.end()), uniq.end());
+  std::vector<double> gcost(uniq.size(), 0.0);
+  std::vector<int> gid(tmp.size());
+  for (size_t k = 0; k < tmp.size(); ++k) {
+    gid[k] = int(std::lower_bound(uniq.begin(), uniq.end(), keys[k]) - uniq.begin());
+    gcost[gid[k]] += tmp[k].cost;
+  }
+  std::vector<int> gorder(uniq.size());
+  for (size_t g = 0; g < uniq.size(); ++g) gorder[g] = int(g);
+  std::stable_sort(gorder.begin(), gorder.end(), [&](int a, int b) {
+    if (uniq[a].cls != uniq[b].cls) return uniq[a].cls < uniq[b].cls;
+    return gcost[a] > gcost[b];
   });
+  P.groups.clear();
   P.class_begin.assign(kNumClasses + 1, 0);
-  for (const Tmp& t : tmp) {
-    P.jobs.push_back(t.j);
-    P.class_begin[t.cls + 1]++;
+  for (int g : gorder) {
+    std::vector<int> members;
+    for (size_t k = 0; k < tmp.size(); ++k)
+      if (gid[k] == g) members.push_back(int(k));
+    std::stable_sort(members.begin(), members.end(), [&](int a, int b) { return tmp[a].cost > tmp[b].cost; });
+    Group G{};
+    G.first_job = int(P.jobs.size());
+    G.n_jobs = int(members.size());
+    G.lanes_log2 = tmp[members[0]].j.lanes_log2;
+    for (int k : members) P.jobs.push_back(tmp[k].j);
+    P.groups.push_back(G);
+    P.class_begin[uniq[g].cls + 1]++;
   }
   for (int c = 0; c < kNumClasses; ++c) P.class_begin[c + 1] += P.class_begin[c];
   P.n_variants = 0;
   for (int u : used) P.n_variants += u;
 }
 
-int tasks_of(const Job& j, int64_t n) {
-  const int s = 64 >> j.lanes_log2;
-  return int((n + s - 1) / s);
+int64_t tasks_of(const Group& g, int64_t n, int edge_slots_log2) {
+  const int sg = std::min(edge_slots_log2, 6 - g.lanes_log2);
+  const int s = 64 >> (g.lanes_log2 + sg);  // receivers per wave
+  return int64_t(g.n_jobs) * ((n + s - 1) / s);
+}
+
+// Edge slots per receiver for this graph size: only when one receiver per lane group
+// would leave SIMDs without a wave (small graphs) are a receiver's edges split over
+// edge slots; each extra wave pays a prologue of dependent loads, which measured
+// slower than a longer edge loop whenever the grid already fills the GPU.
+constexpr int64_t kTargetWaves = 256 * 4;
+int choose_edge_slots_log2(const cgtp_plan_s& P, int64_t n) {
+  for (int sg = 0; sg < 3; ++sg) {
+    int64_t waves = 0;
+    for (const Group& g : P.groups) waves += tasks_of(g, n, sg);
+    if (waves >= kTargetWaves) return sg;
+  }
+  return 3;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// Workspace of the forward and of the exported prepare (one layout, 256-byte aligned
+// sections): per-node degree, order and radix scratch, the wave-task prefix, and the
+// active edge ids, senders and harmonics compacted within each row.
 struct FwdWorkspace {
-  int32_t *act_row_ptr, *act_eid, *act_col, *order, *deg, *tmp_a, *tmp_b, *task_start;
+  int32_t *deg, *order, *tmp_a, *tmp_b, *task_start, *act_e, *act_j;
   float* sh;
   size_t bytes;
 };
@@ -241,14 +302,13 @@ FwdWorkspace carve(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
     off += align256(bytes);
     return r;
   };
-  w.act_row_ptr = reinterpret_cast<int32_t*>(take(size_t(n + 1) * 4));
-  w.act_eid = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
-  w.act_col = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
-  w.order = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.deg = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.order = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.tmp_a = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.tmp_b = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
-  w.task_start = reinterpret_cast<int32_t*>(take((P.jobs.size() + 1) * 4));
+  w.task_start = reinterpret_cast<int32_t*>(take((P.groups.size() + 1) * 4));
+  w.act_e = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
+  w.act_j = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_stride) * 4));
   w.bytes = off;
   return w;
@@ -374,11 +434,16 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
       return fail(CGTP_ERR_NO_DEVICE, "current device is not gfx950");
     }
     P->device = dev;
-    const size_t bytes = P->jobs.size() * sizeof(Job);
-    hipError_t e = hipMalloc(&P->d_jobs, bytes);
-    if (e == hipSuccess) e = hipMemcpy(P->d_jobs, P->jobs.data(), bytes, hipMemcpyHostToDevice);
+    const size_t jb = P->jobs.size() * sizeof(Job), gb = P->groups.size() * sizeof(Group);
+    hipError_t e = hipMalloc(&P->d_tables, jb + gb);
+    if (e == hipSuccess) {
+      P->d_jobs = static_cast<Job*>(P->d_tables);
+      P->d_groups = reinterpret_cast<Group*>(static_cast<char*>(P->d_tables) + jb);
+      e = hipMemcpy(P->d_jobs, P->jobs.data(), jb, hipMemcpyHostToDevice);
+    }
+    if (e == hipSuccess) e = hipMemcpy(P->d_groups, P->groups.data(), gb, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
-      if (P->d_jobs) (void)hipFree(P->d_jobs);
+      if (P->d_tables) (void)hipFree(P->d_tables);
       delete P;
       return fail(CGTP_ERR_HIP, "job table upload: %s", hipGetErrorString(e));
     }
@@ -389,11 +454,11 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
 
 void cgtp_plan_destroy(cgtp_plan_t plan) {
   if (!plan) return;
-  if (plan->d_jobs) {
+  if (plan->d_tables) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != plan->device) (void)hipSetDevice(plan->device);
-    (void)hipFree(plan->d_jobs);
+    (void)hipFree(plan->d_tables);
     if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
   }
   delete plan;
@@ -511,18 +576,19 @@ int cgtp_conv_prepare(cgtp_plan_t P, const int32_t* row_ptr, const uint8_t* mask
     return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, w.bytes);
   if (!aligned(workspace, 256)) return fail(CGTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  CGTP_HIP(launch_prepare_rows(row_ptr, mask, int(n_nodes), w.deg, act_row_ptr, order, w.tmp_a, w.tmp_b, s));
-  EdgeGeom g{};
-  g.row_ptr = row_ptr;
-  g.mask = mask;
-  g.act_row_ptr = act_row_ptr;
-  g.n_nodes = int(n_nodes);
-  g.n_edges = int(n_edges);
-  CGTP_HIP(launch_edge_pass(g, act_eid, nullptr, nullptr, P->l_sh_max, s));
+  RowPass rp{};
+  rp.row_ptr = row_ptr;
+  rp.mask = mask;
+  rp.deg = w.deg;
+  rp.n_nodes = int(n_nodes);
+  rp.n_edges = int(n_edges);
+  CGTP_HIP(launch_rows(rp, P->l_sh_max, s));
+  CGTP_HIP(launch_order(w.deg, int(n_nodes), act_row_ptr, order, w.tmp_a, w.tmp_b, nullptr, 0, 0, nullptr, s));
+  CGTP_HIP(launch_compact(row_ptr, mask, act_row_ptr, int(n_nodes), int(n_edges), act_eid, s));
   return ok();
 }
 
-static void fill_cell(EdgeGeom& g, const float* cell) {
+static void fill_cell(RowPass& g, const float* cell) {
   g.has_cell = cell != nullptr;
   for (int k = 0; k < 9; ++k) g.cell[k] = cell ? double(cell[k]) : 0.0;
 }
@@ -532,22 +598,23 @@ int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float c
   int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
   if (rc != CGTP_OK) return rc;
   if (n_edges > 0 && (!pos || !col || !sh)) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
-  EdgeGeom g{};
+  RowPass g{};
   g.pos = pos;
   g.row_ptr = row_ptr;
   g.col = col;
   g.shift = shift;
-  g.act_row_ptr = row_ptr;
+  g.sh = sh;
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
-  CGTP_HIP(launch_edge_pass(g, nullptr, nullptr, sh, P->l_sh_max, static_cast<hipStream_t>(stream)));
+  CGTP_HIP(launch_rows(g, P->l_sh_max, static_cast<hipStream_t>(stream)));
   return ok();
 }
 
-int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
-                      const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
-                      const uint8_t* mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
+static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
+                             const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
+                             const float* x, const float* w, const uint8_t* mask, float* out, void* workspace,
+                             size_t ws_bytes, void* stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
   if (rc != CGTP_OK) return rc;
   if (n_nodes > 0 && (!out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
@@ -561,30 +628,34 @@ int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const fl
   if (n_nodes == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  // 1. active CSR and node order (BranchIP sparse evaluation; LunaTP Table 9)
-  CGTP_HIP(launch_prepare_rows(row_ptr, mask, int(n_nodes), ws.deg, ws.act_row_ptr, ws.order, ws.tmp_a, ws.tmp_b, s));
-  // 2. compacted active edges and their harmonics
-  EdgeGeom g{};
+  // 1. per row: active degree and the harmonics of its active edges (CSR order)
+  RowPass g{};
   g.pos = pos;
   g.row_ptr = row_ptr;
   g.col = col;
   g.shift = shift;
   g.mask = mask;
-  g.act_row_ptr = ws.act_row_ptr;
+  g.deg = ws.deg;
+  g.act_e = ws.act_e;
+  g.act_j = ws.act_j;
+  g.sh = ws.sh;
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
-  CGTP_HIP(launch_edge_pass(g, ws.act_eid, ws.act_col, ws.sh, P->l_sh_max, s));
-  // 3. wave-task prefix of all jobs for this node count
-  CGTP_HIP(launch_task_prefix(P->d_jobs, int(P->jobs.size()), int(n_nodes), ws.task_start, s));
-  // 4. the fused convolution, one launch per kernel class present in the plan
+  CGTP_HIP(launch_rows(g, P->l_sh_max, s));
+  // 2. node order by active degree (LunaTP Table 9) and the wave-task prefix
+  const int sg = choose_edge_slots_log2(*P, n_nodes);
+  CGTP_HIP(launch_order(ws.deg, int(n_nodes), nullptr, ws.order, ws.tmp_a, ws.tmp_b, P->d_groups,
+                        int(P->groups.size()), sg, ws.task_start, s));
+  // 3. the fused convolution, one launch per kernel class present in the plan
   ConvArgs a{};
   a.x = x;
   a.w = w;
   a.sh = ws.sh;
-  a.act_row_ptr = ws.act_row_ptr;
-  a.act_eid = ws.act_eid;
-  a.act_col = ws.act_col;
+  a.row_ptr = row_ptr;
+  a.act_e = ws.act_e;
+  a.act_j = ws.act_j;
+  a.deg = ws.deg;
   a.order = ws.order;
   a.out = out;
   a.n_nodes = int(n_nodes);
@@ -592,19 +663,48 @@ int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const fl
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
   a.sh_stride = P->sh_stride;
+  a.edge_slots_log2 = sg;
+  int first_cls = -1, last_cls = -1;
+  for (int c = 0; c < kNumClasses; ++c)
+    if (P->class_begin[c] != P->class_begin[c + 1]) {
+      if (first_cls < 0) first_cls = c;
+      last_cls = c;
+    }
   for (int c = 0; c < kNumClasses; ++c) {
     const int b = P->class_begin[c], e = P->class_begin[c + 1];
     if (b == e) continue;
     int64_t tasks = 0;
-    for (int k = b; k < e; ++k) tasks += tasks_of(P->jobs[k], n_nodes);
+    for (int k = b; k < e; ++k) tasks += tasks_of(P->groups[k], n_nodes, sg);
     if (tasks > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many wave tasks");
-    a.jobs = P->d_jobs + b;
+    a.jobs = P->d_jobs;
+    a.groups = P->d_groups + b;
     a.task_start = ws.task_start + b;
-    a.n_jobs = e - b;
+    a.n_groups = e - b;
     a.total_tasks = int(tasks);
-    CGTP_HIP(launch_conv(a, c, s));
+    CGTP_HIP(launch_conv(a, c, s, c == first_cls ? ev_begin : nullptr, c == last_cls ? ev_end : nullptr));
+  }
+  if (first_cls < 0) {  // no wave task (cannot happen with n_nodes > 0): keep the events valid
+    if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
+    if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));
   }
   return ok();
+}
+
+int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
+                      const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
+                      const uint8_t* mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
+  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, out, workspace,
+                           ws_bytes, stream, nullptr, nullptr);
+}
+
+int cgtp_conv_forward_timed(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
+                            const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
+                            const float* x, const float* w, const uint8_t* mask, float* out, void* workspace,
+                            size_t ws_bytes, void* stream, void* ev_conv_begin, void* ev_conv_end) {
+  if (!ev_conv_begin || !ev_conv_end) return fail(CGTP_ERR_INVALID_ARG, "events must not be NULL");
+  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, out, workspace,
+                           ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
+                           static_cast<hipEvent_t>(ev_conv_end));
 }
 
 }  // extern "C"

@@ -12,13 +12,13 @@ namespace cgtp {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxShL = kMaxL;       // harmonics up to l = 6
 
-// One wave job: a path p and a block of its channels.  A wave runs one job for S
-// consecutive nodes of the degree-sorted node order; 2^lanes_log2 lanes
-// serve one node, each lane owning K consecutive channels.  (LunaTP Figure 3(b): paths
-// mapped to SIMD lanes by channel block; here sized to the 64-lane wavefront.)
+// One wave job: a path p and a block of its channels.  A wave runs one job for
+// S = 64 / 2^lanes_log2 consecutive receivers of the degree-sorted order; 2^lanes_log2
+// lanes serve one receiver, each lane owning K consecutive channels.  (LunaTP Figure
+// 3(b): paths mapped to SIMD lanes by channel block; sized to the 64-lane wavefront.)
 struct Job {
   int32_t variant;     // index of the (l1, l2, l3, K) specialisation
-  int32_t lanes_log2;  // log2 of the lanes serving one node (lanes <= 64)
+  int32_t lanes_log2;  // log2 of the lanes serving one receiver (<= 64)
   int32_t n_ch;      // channels in this job (multiple of K)
   int32_t in_off;    // float offset of the job's first channel in a row of x
   int32_t out_off;   // float offset of the job's first channel in a row of out
@@ -28,25 +28,39 @@ struct Job {
 };
 static_assert(sizeof(Job) == 32, "Job is 32 bytes");
 
+// A group: the jobs of one input irrep, one channel block and one kernel class.  They
+// read the same columns of x and use the same lanes per receiver, so their tasks are
+// interleaved (node group major, job minor): the waves of one workgroup then run
+// different paths on the same receivers and share the gathered x_j rows in the CU's L1
+// cache (LunaTP Table 8: cross-path input reuse).
+struct Group {
+  int32_t first_job;   // index into the plan's job table
+  int32_t n_jobs;
+  int32_t lanes_log2;
+  int32_t pad;
+};
+
 struct ConvArgs {
   const float* x;
   const float* w;
-  const float* sh;
-  const int32_t* act_row_ptr;
-  const int32_t* act_eid;
-  const int32_t* act_col;
-  const int32_t* order;
-  const int32_t* task_start;  // [n_jobs + 1] prefix of wave tasks per job (device)
+  const float* sh;            // harmonics of active edges, compacted within each row
+  const int32_t* row_ptr;     // receiver CSR
+  const int32_t* act_e;       // active edge ids, compacted within each row (at row_ptr[i] + q)
+  const int32_t* act_j;       // their senders
+  const int32_t* deg;         // active edges per row
+  const int32_t* order;       // nodes by active degree, descending
+  const int32_t* task_start;  // prefix of wave tasks per group, from this launch's first group
   float* out;
-  const Job* jobs;            // first job of this launch
+  const Job* jobs;            // the plan's job table
+  const Group* groups;        // first group of this launch
   int32_t n_nodes;
   int32_t f_in;
   int32_t f_out;
   int32_t w_stride;
   int32_t sh_stride;
-  int32_t n_jobs;
+  int32_t n_groups;
   int32_t total_tasks;
-  int32_t pad;
+  int32_t edge_slots_log2;    // requested edge slots per receiver (clamped per job)
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

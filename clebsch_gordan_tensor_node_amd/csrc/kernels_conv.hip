@@ -7,5 +7,6 @@
 #endif
 
 namespace cgtp {
-template hipError_t launch_conv_class<CGTP_CONV_CLASS>(const ConvArgs& args, hipStream_t s);
+template hipError_t launch_conv_class<CGTP_CONV_CLASS>(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start,
+                                                       hipEvent_t ev_stop);
 }  // namespace cgtp

@@ -16,6 +16,7 @@ namespace cgtp {
 namespace {
 
 constexpr int kScanThreads = 1024;
+constexpr int kDegCache = 8192;
 constexpr int kScanWaves = kScanThreads / kWave;
 
 __device__ inline int lane_id() { return __lane_id(); }
@@ -213,39 +214,52 @@ __global__ void nbr_fill_kernel(const float* __restrict__ pos, int n, GridArgs g
 // Mask prepare.
 // ---------------------------------------------------------------------------------
 
-__global__ void prep_count_kernel(const int32_t* __restrict__ row_ptr, const uint8_t* __restrict__ mask,
-                                  int n, int32_t* __restrict__ deg) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int beg = row_ptr[i], end = row_ptr[i + 1];
-  int d = end - beg;
-  if (mask) {
-    d = 0;
-    for (int e = beg; e < end; ++e) d += (mask[e] != 0);
-  }
-  deg[i] = d;
-}
-
-// One workgroup: act_row_ptr = exclusive scan of deg; order = node ids sorted by deg
-// descending, ties by id ascending (stable LSD radix sort on maxdeg - deg, 8-bit
-// digits, ranks inside a wave from ballots, across waves from an LDS table).
+// One workgroup: act_row_ptr = exclusive scan of deg (if requested); order = node ids
+// sorted by deg descending, ties by id ascending (stable LSD radix sort on
+// maxdeg - deg, 8-bit digits, ranks inside a wave from ballots, across waves from an
+// LDS table); task_start = wave-task prefix of the plan's job groups (if requested).
+// Degrees are cached in LDS when n <= kDegCache, so each radix pass reads LDS only.
 __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int32_t* __restrict__ deg, int n,
                                                                       int32_t* __restrict__ act_row_ptr,
                                                                       int32_t* __restrict__ order,
                                                                       int32_t* __restrict__ tmp_a,
-                                                                      int32_t* __restrict__ tmp_b) {
+                                                                      int32_t* __restrict__ tmp_b,
+                                                                      const Group* __restrict__ groups, int n_groups,
+                                                                      int edge_slots_log2,
+                                                                      int32_t* __restrict__ task_start) {
   __shared__ int wsum[kScanWaves + 1];
   __shared__ int s_max;
   __shared__ int hist[256];
   __shared__ int base[256];
   __shared__ int tile_tot[256];
   __shared__ int wcnt[kScanWaves][256];
+  __shared__ int s_deg[kDegCache];
 
   const int tid = threadIdx.x;
+  const bool cached = n <= kDegCache;
   const int lane = lane_id();
   const int wave = tid / kWave;
 
-  // 1. scan and maximum
+  if (task_start) {  // uniform
+    int run = 0;
+    for (int b0 = 0; b0 < n_groups; b0 += kScanThreads) {
+      const int k = b0 + tid;
+      int v = 0;
+      if (k < n_groups) {
+        const int lg = groups[k].lanes_log2;
+        const int sg = edge_slots_log2 < 6 - lg ? edge_slots_log2 : 6 - lg;
+        const int s = 64 >> (lg + sg);  // receivers per wave
+        v = groups[k].n_jobs * ((n + s - 1) / s);
+      }
+      int total;
+      const int ex = block_exclusive_scan(v, wsum, total);
+      if (k < n_groups) task_start[k] = run + ex;
+      run += total;
+    }
+    if (tid == 0) task_start[n_groups] = run;
+  }
+
+  // 1. scan (optional) and maximum
   if (tid == 0) s_max = 0;
   __syncthreads();
   int carry = 0;
@@ -253,13 +267,16 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
   for (int b0 = 0; b0 < n; b0 += kScanThreads) {
     const int idx = b0 + tid;
     const int v = idx < n ? deg[idx] : 0;
+    if (cached && idx < n) s_deg[idx] = v;
     local_max = v > local_max ? v : local_max;
-    int total;
-    const int ex = block_exclusive_scan(v, wsum, total);
-    if (idx < n) act_row_ptr[idx] = carry + ex;
-    carry += total;
+    if (act_row_ptr) {
+      int total;
+      const int ex = block_exclusive_scan(v, wsum, total);
+      if (idx < n) act_row_ptr[idx] = carry + ex;
+      carry += total;
+    }
   }
-  if (tid == 0) act_row_ptr[n] = carry;
+  if (act_row_ptr && tid == 0) act_row_ptr[n] = carry;
   atomicMax(&s_max, local_max);
   __syncthreads();
   const int maxdeg = s_max;
@@ -280,23 +297,21 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
     __syncthreads();
     for (int idx = tid; idx < n; idx += kScanThreads) {
       const int id = src ? src[idx] : idx;
-      const int digit = ((maxdeg - deg[id]) >> shift) & 255;
+      const int digit = ((maxdeg - (cached ? s_deg[id] : deg[id])) >> shift) & 255;
       atomicAdd(&hist[digit], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int run = 0;
-      for (int k = 0; k < 256; ++k) {
-        base[k] = run;
-        run += hist[k];
-      }
+    {
+      int total;
+      const int ex = block_exclusive_scan(tid < 256 ? hist[tid] : 0, wsum, total);
+      if (tid < 256) base[tid] = ex;
     }
     __syncthreads();
     for (int b0 = 0; b0 < n; b0 += kScanThreads) {
       const int idx = b0 + tid;
       const bool valid = idx < n;
       const int id = valid ? (src ? src[idx] : idx) : 0;
-      const int digit = valid ? (((maxdeg - deg[id]) >> shift) & 255) : 0;
+      const int digit = valid ? (((maxdeg - (cached ? s_deg[id] : deg[id])) >> shift) & 255) : 0;
       unsigned long long same = __ballot(valid);
 #pragma unroll
       for (int bit = 0; bit < 8; ++bit) {
@@ -329,85 +344,102 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
 }
 
 // ---------------------------------------------------------------------------------
-// Per-edge pass: receiver by binary search over row_ptr; position among the active
-// edges of the row; compacted ids; edge vector and harmonics in fp64.
+// Per-row pass (one wave per receiver row, lanes over its edges): active-edge count and
+// the real harmonics of every active edge, stored in CSR edge order.  Geometry and
+// harmonics in fp64, stored fp32.
 // ---------------------------------------------------------------------------------
 
-struct EdgeArgs {
+struct RowArgs {
   const float* pos;
   const int32_t* row_ptr;
   const int32_t* col;
   const int8_t* shift;
   const uint8_t* mask;
-  const int32_t* act_row_ptr;
-  int32_t* act_eid;
-  int32_t* act_col;
-  float* sh;
+  int32_t* deg;    // may be null
+  int32_t* act_e;  // may be null
+  int32_t* act_j;  // may be null
+  float* sh;       // may be null
   int n_nodes;
-  int n_edges;
   int has_cell;
   int sh_stride;
   double cell[9];
 };
 
-template <int L>
-__global__ void edge_pass_kernel(EdgeArgs a) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= a.n_edges) return;
-  if (a.mask && a.mask[e] == 0) return;
-  int lo = 0, hi = a.n_nodes;  // find i with row_ptr[i] <= e < row_ptr[i+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.row_ptr[mid] <= e) lo = mid; else hi = mid;
-  }
-  const int i = lo;
-  const int rbeg = a.row_ptr[i];
-  int pos_in_row = e - rbeg;
-  if (a.mask) {
-    pos_in_row = 0;
-    for (int q = rbeg; q < e; ++q) pos_in_row += (a.mask[q] != 0);
-  }
-  const int slot = a.act_row_ptr[i] + pos_in_row;
-  if (a.act_eid) a.act_eid[slot] = e;
-  if (!a.act_col && !a.sh) return;  // col (and pos) are only needed by these outputs
-  const int j = a.col[e];
-  if (a.act_col) a.act_col[slot] = j;
-  if (!a.sh) return;
+constexpr int kRowThreads = 256;
 
-  double r[3];
+// Row i's active edges are written compacted within the row's own CSR segment: the
+// q-th active edge of row i goes to slot row_ptr[i] + q (q from a ballot prefix).  With
+// no mask the slot is the edge itself.
+template <int L>
+__global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
+  const int row = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kRowThreads / kWave) + int(threadIdx.x) / kWave);
+  if (row >= a.n_nodes) return;
+  const int lane = lane_id();
+  const unsigned long long lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+  const int rb = a.row_ptr[row], re = a.row_ptr[row + 1];
+  const double pi0 = a.pos ? a.pos[3 * row + 0] : 0.0;
+  const double pi1 = a.pos ? a.pos[3 * row + 1] : 0.0;
+  const double pi2 = a.pos ? a.pos[3 * row + 2] : 0.0;
+  int cnt = 0;
+  for (int b0 = rb; b0 < re; b0 += kWave) {
+    const int e = b0 + lane;
+    const bool act = e < re && (!a.mask || a.mask[e] != 0);
+    const unsigned long long bal = __ballot(act);
+    const int slot = rb + cnt + __popcll(bal & lt_mask);
+    cnt += __popcll(bal);
+    if (!act) continue;
+    const int j = (a.act_j || a.sh) ? a.col[e] : 0;
+    if (a.act_e) a.act_e[slot] = e;
+    if (a.act_j) a.act_j[slot] = j;
+    if (!a.sh) continue;
+    double r[3] = {double(a.pos[3 * j + 0]) - pi0, double(a.pos[3 * j + 1]) - pi1, double(a.pos[3 * j + 2]) - pi2};
+    if (a.has_cell && a.shift) {
+      const double s0 = a.shift[3 * e + 0], s1 = a.shift[3 * e + 1], s2 = a.shift[3 * e + 2];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) r[k] = double(a.pos[3 * j + k]) - double(a.pos[3 * i + k]);
-  if (a.has_cell && a.shift) {
-    const double s0 = a.shift[3 * e + 0], s1 = a.shift[3 * e + 1], s2 = a.shift[3 * e + 2];
+      for (int k = 0; k < 3; ++k) r[k] = r[k] + s0 * a.cell[k] + s1 * a.cell[3 + k] + s2 * a.cell[6 + k];
+    }
+    const double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+    constexpr int NY = (L + 1) * (L + 1);
+    double Y[NY];
+    if (rr > 0.0) {
+      const double inv = 1.0 / rr;
+      sh_unit<L>(r[0] * inv, r[1] * inv, r[2] * inv, Y);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 3; ++k) r[k] = r[k] + s0 * a.cell[k] + s1 * a.cell[3 + k] + s2 * a.cell[6 + k];
+      for (int q = 0; q < NY; ++q) Y[q] = 0.0;
+      Y[0] = 1.0;
+    }
+    float* out = a.sh + (long)slot * a.sh_stride;
+#pragma unroll
+    for (int q = 0; q < NY; ++q) out[q] = float(Y[q]);
   }
-  const double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
-  constexpr int NY = (L + 1) * (L + 1);
-  double Y[NY];
-  if (rr > 0.0) {
-    const double inv = 1.0 / rr;
-    sh_unit<L>(r[0] * inv, r[1] * inv, r[2] * inv, Y);
-  } else {
-#pragma unroll
-    for (int q = 0; q < NY; ++q) Y[q] = 0.0;
-    Y[0] = 1.0;
-  }
-  float* out = a.sh + (long)slot * a.sh_stride;
-#pragma unroll
-  for (int q = 0; q < NY; ++q) out[q] = float(Y[q]);
+  if (a.deg && lane == 0) a.deg[row] = cnt;
 }
 
-__global__ void task_prefix_kernel(const Job* __restrict__ jobs, int n_jobs, int n_nodes,
-                                   int32_t* __restrict__ task_start) {
-  if (threadIdx.x != 0) return;
-  int run = 0;
-  for (int k = 0; k < n_jobs; ++k) {
-    task_start[k] = run;
-    const int s = 64 >> jobs[k].lanes_log2;
-    run += (n_nodes + s - 1) / s;
+// ---------------------------------------------------------------------------------
+// Compaction of the active edges (ids in CSR order) for the exported prepare: the
+// receiver of each edge by binary search over row_ptr, its rank among the active
+// edges of its row, and the slot act_row_ptr[i] + rank.
+// ---------------------------------------------------------------------------------
+
+__global__ void compact_kernel(const int32_t* __restrict__ row_ptr, const uint8_t* __restrict__ mask,
+                               const int32_t* __restrict__ act_row_ptr, int n_nodes, int n_edges,
+                               int32_t* __restrict__ act_eid) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_edges) return;
+  if (mask && mask[e] == 0) return;
+  int lo = 0, hi = n_nodes;  // find i with row_ptr[i] <= e < row_ptr[i+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (row_ptr[mid] <= e) lo = mid; else hi = mid;
   }
-  task_start[n_jobs] = run;
+  const int rbeg = row_ptr[lo];
+  int rank = e - rbeg;
+  if (mask) {
+    rank = 0;
+    for (int q = rbeg; q < e; ++q) rank += (mask[q] != 0);
+  }
+  act_eid[act_row_ptr[lo] + rank] = e;
 }
 
 }  // namespace
@@ -494,70 +526,70 @@ hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrW
   return hipGetLastError();
 }
 
-hipError_t launch_prepare_rows(const int32_t* row_ptr, const uint8_t* mask, int n, int32_t* deg,
-                               int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a, int32_t* tmp_b,
-                               hipStream_t s) {
-  const int tb = 256;
-  if (n > 0) prep_count_kernel<<<ceil_div(n, tb), tb, 0, s>>>(row_ptr, mask, n, deg);
-  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, act_row_ptr, order, tmp_a, tmp_b);
-  return hipGetLastError();
-}
-
-hipError_t launch_edge_pass(const EdgeGeom& g, int32_t* act_eid, int32_t* act_col, float* sh, int l_sh_max,
-                            hipStream_t s) {
-  if (g.n_edges == 0 || g.n_nodes == 0) return hipSuccess;
-  if (!g.row_ptr || !g.act_row_ptr) return hipErrorInvalidValue;
-  if ((act_col || sh) && !g.col) return hipErrorInvalidValue;
-  if (sh && !g.pos) return hipErrorInvalidValue;
-  EdgeArgs a{};
-  a.pos = g.pos;
-  a.row_ptr = g.row_ptr;
-  a.col = g.col;
-  a.shift = g.shift;
-  a.mask = g.mask;
-  a.act_row_ptr = g.act_row_ptr;
-  a.act_eid = act_eid;
-  a.act_col = act_col;
-  a.sh = sh;
-  a.n_nodes = g.n_nodes;
-  a.n_edges = g.n_edges;
-  a.has_cell = g.has_cell;
+hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
+  if (p.n_nodes == 0) return hipSuccess;
+  if (!p.row_ptr) return hipErrorInvalidValue;
+  if ((p.sh || p.act_j) && p.n_edges > 0 && !p.col) return hipErrorInvalidValue;
+  if (p.sh && p.n_edges > 0 && !p.pos) return hipErrorInvalidValue;
+  RowArgs a{};
+  a.pos = p.pos;
+  a.row_ptr = p.row_ptr;
+  a.col = p.col;
+  a.shift = p.shift;
+  a.mask = p.mask;
+  a.deg = p.deg;
+  a.act_e = p.act_e;
+  a.act_j = p.act_j;
+  a.sh = p.sh;
+  a.n_nodes = p.n_nodes;
+  a.has_cell = p.has_cell;
   a.sh_stride = (l_sh_max + 1) * (l_sh_max + 1);
-  for (int k = 0; k < 9; ++k) a.cell[k] = g.cell[k];
-  const int tb = 256;
-  const int nb = ceil_div(g.n_edges, tb);
+  for (int k = 0; k < 9; ++k) a.cell[k] = p.cell[k];
+  const int nb = ceil_div(p.n_nodes, kRowThreads / kWave);
   switch (l_sh_max) {
-    case 0: edge_pass_kernel<0><<<nb, tb, 0, s>>>(a); break;
-    case 1: edge_pass_kernel<1><<<nb, tb, 0, s>>>(a); break;
-    case 2: edge_pass_kernel<2><<<nb, tb, 0, s>>>(a); break;
-    case 3: edge_pass_kernel<3><<<nb, tb, 0, s>>>(a); break;
-    case 4: edge_pass_kernel<4><<<nb, tb, 0, s>>>(a); break;
-    case 5: edge_pass_kernel<5><<<nb, tb, 0, s>>>(a); break;
-    case 6: edge_pass_kernel<6><<<nb, tb, 0, s>>>(a); break;
+    case 0: edge_rows_kernel<0><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 1: edge_rows_kernel<1><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 2: edge_rows_kernel<2><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 3: edge_rows_kernel<3><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 4: edge_rows_kernel<4><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 5: edge_rows_kernel<5><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 6: edge_rows_kernel<6><<<nb, kRowThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_task_prefix(const Job* jobs, int n_jobs, int n_nodes, int32_t* task_start, hipStream_t s) {
-  task_prefix_kernel<<<1, 64, 0, s>>>(jobs, n_jobs, n_nodes, task_start);
+hipError_t launch_order(const int32_t* deg, int n, int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
+                        int32_t* tmp_b, const Group* groups, int n_groups, int edge_slots_log2, int32_t* task_start,
+                        hipStream_t s) {
+  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, act_row_ptr, order, tmp_a, tmp_b, groups, n_groups,
+                                                    edge_slots_log2, task_start);
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const ConvArgs& args, int variant_class, hipStream_t s) {
-  switch (variant_class) {
-    case 0: return launch_conv_class<0>(args, s);
-    case 1: return launch_conv_class<1>(args, s);
-    case 2: return launch_conv_class<2>(args, s);
-    case 3: return launch_conv_class<3>(args, s);
-    case 4: return launch_conv_class<4>(args, s);
-    case 5: return launch_conv_class<5>(args, s);
-    case 6: return launch_conv_class<6>(args, s);
-    case 7: return launch_conv_class<7>(args, s);
+hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int32_t* act_row_ptr, int n_nodes,
+                          int n_edges, int32_t* act_eid, hipStream_t s) {
+  if (n_edges == 0 || n_nodes == 0) return hipSuccess;
+  const int tb = 256;
+  compact_kernel<<<ceil_div(n_edges, tb), tb, 0, s>>>(row_ptr, mask, act_row_ptr, n_nodes, n_edges, act_eid);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const ConvArgs& args, int cls, hipStream_t s, hipEvent_t b, hipEvent_t e) {
+  switch (cls) {
+    case 0: return launch_conv_class<0>(args, s, b, e);
+    case 1: return launch_conv_class<1>(args, s, b, e);
+    case 2: return launch_conv_class<2>(args, s, b, e);
+    case 3: return launch_conv_class<3>(args, s, b, e);
+    case 4: return launch_conv_class<4>(args, s, b, e);
+    case 5: return launch_conv_class<5>(args, s, b, e);
+    case 6: return launch_conv_class<6>(args, s, b, e);
+    case 7: return launch_conv_class<7>(args, s, b, e);
+    case 8: return launch_conv_class<8>(args, s, b, e);
     default: return hipErrorInvalidValue;
   }
 }
 
-static_assert(kNumClasses == 8, "launch_conv covers every kernel class");
+static_assert(kNumClasses == 9, "launch_conv covers every kernel class");
 
 }  // namespace cgtp

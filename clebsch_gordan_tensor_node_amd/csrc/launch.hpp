@@ -35,37 +35,42 @@ hipError_t launch_nbr_count(const float* pos, int n, const NbrGrid& g, const Nbr
 hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrWorkspace& w,
                            const int32_t* row_ptr, int32_t* col, int8_t* shift, hipStream_t s);
 
-// Mask prepare: per-row active counts -> act_row_ptr (scan) and node order.
-// deg, tmp_a, tmp_b: [n] int32 scratch.
-hipError_t launch_prepare_rows(const int32_t* row_ptr, const uint8_t* mask, int n, int32_t* deg,
-                               int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
-                               int32_t* tmp_b, hipStream_t s);
-
-// Per-edge pass: compacted active-edge arrays and/or edge harmonics.
-// act_eid, act_col, sh may each be null.  cell null = open boundaries.
-struct EdgeGeom {
+// Per-row pass: active-edge count per row and, compacted within each row's CSR segment,
+// the active edge ids, senders and harmonics (sh [n_edges, (l_sh_max+1)^2]).  Every
+// output may be null.  Without a mask the slots are the edges themselves.
+struct RowPass {
   const float* pos;
   const int32_t* row_ptr;
   const int32_t* col;
   const int8_t* shift;
   const uint8_t* mask;
-  const int32_t* act_row_ptr;
+  int32_t* deg;
+  int32_t* act_e;  // active edge ids compacted within each row (at row_ptr[i] + q)
+  int32_t* act_j;  // their senders
+  float* sh;       // their harmonics, same slots
   int n_nodes;
   int n_edges;
   int has_cell;
   double cell[9];
 };
-hipError_t launch_edge_pass(const EdgeGeom& g, int32_t* act_eid, int32_t* act_col, float* sh,
-                            int l_sh_max, hipStream_t s);
+hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s);
+
+// One workgroup: optional exclusive scan of deg into act_row_ptr, node order by deg
+// descending (ties by id), optional wave-task prefix of the job groups into task_start.
+// tmp_a, tmp_b: [n] int32 scratch.
+hipError_t launch_order(const int32_t* deg, int n, int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
+                        int32_t* tmp_b, const Group* groups, int n_groups, int edge_slots_log2, int32_t* task_start,
+                        hipStream_t s);
+
+// Ids of the active edges in CSR order, at act_row_ptr[i] + rank within row i.
+hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int32_t* act_row_ptr, int n_nodes,
+                          int n_edges, int32_t* act_eid, hipStream_t s);
 
 // The fused conv kernel of one variant class over `args.total_tasks` wave tasks
 // (one explicit instantiation per class, each in its own translation unit).
+// ev_start / ev_stop (may be null): HIP events stamped at this launch's start / end.
 template <int C>
-hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s);
-hipError_t launch_conv(const ConvArgs& args, int variant_class, hipStream_t s);
-
-// Wave-task prefix of the jobs of one launch, on the device:
-// task_start[k] = sum_{q<k} ceil(n_nodes / (64 >> jobs[q].lanes_log2)).
-hipError_t launch_task_prefix(const Job* jobs, int n_jobs, int n_nodes, int32_t* task_start, hipStream_t s);
+hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_conv(const ConvArgs& args, int cls, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 
 }  // namespace cgtp

@@ -50,15 +50,30 @@ constexpr int variant_index(int l1, int l2, int l3, int k) {
   return -1;
 }
 
-constexpr int kSmallLMax = 3;
-// Kernel class: 0 = every l <= 3; 1 + l1 otherwise.  Each class is a separate kernel
-// built in its own translation unit, so the register budget of small-l code is not set
-// by large-l code and the classes compile in parallel.
-constexpr int variant_class(int v) {
+constexpr int variant_lmax(int v) {
   const VariantDesc d = variant_desc(v);
-  const int m = d.l1 > d.l2 ? (d.l1 > d.l3 ? d.l1 : d.l3) : (d.l2 > d.l3 ? d.l2 : d.l3);
-  return m <= kSmallLMax ? 0 : 1 + d.l1;
+  const int m = d.l1 > d.l2 ? d.l1 : d.l2;
+  return m > d.l3 ? m : d.l3;
 }
-constexpr int kNumClasses = 2 + kMaxL;
+
+// Kernel classes, each a separate kernel built in its own translation unit (so that
+// the register budget of small-l code is not set by large-l code, and the classes
+// compile in parallel):
+//   0: every variant with l <= 2        (plans whose largest l is 2 or less)
+//   1: every variant with l <= 3        (l <= 3 jobs of plans that reach l = 3 or more)
+//   2 + l1: variants with some l >= 4 and that l1
+constexpr int kNumClasses = 2 + kMaxL + 1;
+constexpr bool class_contains(int c, int v) {
+  const int m = variant_lmax(v);
+  if (c == 0) return m <= 2;
+  if (c == 1) return m <= 3;
+  return m >= 4 && variant_desc(v).l1 == c - 2;
+}
+// class of a variant inside a plan whose largest l is plan_lmax
+constexpr int job_class(int v, int plan_lmax) {
+  const int m = variant_lmax(v);
+  if (m >= 4) return 2 + variant_desc(v).l1;
+  return plan_lmax <= 2 ? 0 : 1;
+}
 
 }  // namespace cgtp
