@@ -149,9 +149,8 @@ struct cgtp_plan_s {
   int n_variants = 0;
   bool host_only = true;
   int device = -1;
-  void* d_tables = nullptr;          // device copy: jobs, then groups
+  void* d_tables = nullptr;          // device copy of the job table
   Job* d_jobs = nullptr;
-  Group* d_groups = nullptr;
 };
 
 namespace {
@@ -285,10 +284,12 @@ int choose_edge_slots_log2(const cgtp_plan_s& P, int64_t n) {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 // Workspace of the forward and of the exported prepare (one layout, 256-byte aligned
-// sections): per-node degree, order and radix scratch, the wave-task prefix, and the
-// active edge ids, senders and harmonics compacted within each row.
+// sections): per-node degree, the position-indexed node records of the degree order,
+// radix scratch, and the active edge ids, senders and harmonics compacted within each
+// row.
 struct FwdWorkspace {
-  int32_t *deg, *order, *tmp_a, *tmp_b, *task_start, *act_e, *act_j;
+  int32_t *deg, *tmp_a, *tmp_b, *act_e, *act_j;
+  int4* node_info;
   float* sh;
   size_t bytes;
 };
@@ -303,10 +304,9 @@ FwdWorkspace carve(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
     return r;
   };
   w.deg = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
-  w.order = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.node_info = reinterpret_cast<int4*>(take(size_t(n) * 16));
   w.tmp_a = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.tmp_b = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
-  w.task_start = reinterpret_cast<int32_t*>(take((P.groups.size() + 1) * 4));
   w.act_e = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.act_j = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_stride) * 4));
@@ -434,14 +434,12 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
       return fail(CGTP_ERR_NO_DEVICE, "current device is not gfx950");
     }
     P->device = dev;
-    const size_t jb = P->jobs.size() * sizeof(Job), gb = P->groups.size() * sizeof(Group);
-    hipError_t e = hipMalloc(&P->d_tables, jb + gb);
+    const size_t jb = P->jobs.size() * sizeof(Job);
+    hipError_t e = hipMalloc(&P->d_tables, jb);
     if (e == hipSuccess) {
       P->d_jobs = static_cast<Job*>(P->d_tables);
-      P->d_groups = reinterpret_cast<Group*>(static_cast<char*>(P->d_tables) + jb);
       e = hipMemcpy(P->d_jobs, P->jobs.data(), jb, hipMemcpyHostToDevice);
     }
-    if (e == hipSuccess) e = hipMemcpy(P->d_groups, P->groups.data(), gb, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       if (P->d_tables) (void)hipFree(P->d_tables);
       delete P;
@@ -583,7 +581,7 @@ int cgtp_conv_prepare(cgtp_plan_t P, const int32_t* row_ptr, const uint8_t* mask
   rp.n_nodes = int(n_nodes);
   rp.n_edges = int(n_edges);
   CGTP_HIP(launch_rows(rp, P->l_sh_max, s));
-  CGTP_HIP(launch_order(w.deg, int(n_nodes), act_row_ptr, order, w.tmp_a, w.tmp_b, nullptr, 0, 0, nullptr, s));
+  CGTP_HIP(launch_order(w.deg, int(n_nodes), row_ptr, act_row_ptr, order, nullptr, w.tmp_a, w.tmp_b, s));
   CGTP_HIP(launch_compact(row_ptr, mask, act_row_ptr, int(n_nodes), int(n_edges), act_eid, s));
   return ok();
 }
@@ -643,46 +641,50 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
   CGTP_HIP(launch_rows(g, P->l_sh_max, s));
-  // 2. node order by active degree (LunaTP Table 9) and the wave-task prefix
+  // 2. node order by active degree (LunaTP Table 9), as position-indexed node records
   const int sg = choose_edge_slots_log2(*P, n_nodes);
-  CGTP_HIP(launch_order(ws.deg, int(n_nodes), nullptr, ws.order, ws.tmp_a, ws.tmp_b, P->d_groups,
-                        int(P->groups.size()), sg, ws.task_start, s));
-  // 3. the fused convolution, one launch per kernel class present in the plan
+  CGTP_HIP(launch_order(ws.deg, int(n_nodes), row_ptr, nullptr, nullptr, ws.node_info, ws.tmp_a, ws.tmp_b, s));
+  // 3. the fused convolution: per kernel class, launches of up to kMaxGroupsPerLaunch
+  //    job groups whose task ranges travel in the kernel arguments
   ConvArgs a{};
   a.x = x;
   a.w = w;
   a.sh = ws.sh;
-  a.row_ptr = row_ptr;
+  a.node_info = ws.node_info;
   a.act_e = ws.act_e;
   a.act_j = ws.act_j;
-  a.deg = ws.deg;
-  a.order = ws.order;
   a.out = out;
+  a.jobs = P->d_jobs;
   a.n_nodes = int(n_nodes);
   a.f_in = int(P->f_in);
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
   a.sh_stride = P->sh_stride;
   a.edge_slots_log2 = sg;
-  int first_cls = -1, last_cls = -1;
+  struct Launch {
+    int cls, g0, g1;
+  };
+  std::vector<Launch> launches;
   for (int c = 0; c < kNumClasses; ++c)
-    if (P->class_begin[c] != P->class_begin[c + 1]) {
-      if (first_cls < 0) first_cls = c;
-      last_cls = c;
-    }
-  for (int c = 0; c < kNumClasses; ++c) {
-    const int b = P->class_begin[c], e = P->class_begin[c + 1];
-    if (b == e) continue;
+    for (int g0 = P->class_begin[c]; g0 < P->class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
+      launches.push_back(Launch{c, g0, std::min(P->class_begin[c + 1], g0 + kMaxGroupsPerLaunch)});
+  for (size_t li = 0; li < launches.size(); ++li) {
+    const Launch& L = launches[li];
     int64_t tasks = 0;
-    for (int k = b; k < e; ++k) tasks += tasks_of(P->groups[k], n_nodes, sg);
+    a.n_groups = L.g1 - L.g0;
+    for (int k = L.g0; k < L.g1; ++k) {
+      const Group& G = P->groups[k];
+      a.g_start[k - L.g0] = int(tasks);
+      a.g_first_job[k - L.g0] = G.first_job;
+      a.g_n_jobs[k - L.g0] = G.n_jobs;
+      a.g_lanes_log2[k - L.g0] = G.lanes_log2;
+      tasks += tasks_of(G, n_nodes, sg);
+    }
     if (tasks > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many wave tasks");
-    a.jobs = P->d_jobs;
-    a.groups = P->d_groups + b;
-    a.task_start = ws.task_start + b;
-    a.n_groups = e - b;
     a.total_tasks = int(tasks);
-    CGTP_HIP(launch_conv(a, c, s, c == first_cls ? ev_begin : nullptr, c == last_cls ? ev_end : nullptr));
+    CGTP_HIP(launch_conv(a, L.cls, s, li == 0 ? ev_begin : nullptr, li + 1 == launches.size() ? ev_end : nullptr));
   }
+  const int first_cls = launches.empty() ? -1 : launches.front().cls;
   if (first_cls < 0) {  // no wave task (cannot happen with n_nodes > 0): keep the events valid
     if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
     if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));

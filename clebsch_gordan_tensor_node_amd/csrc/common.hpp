@@ -40,27 +40,31 @@ struct Group {
   int32_t pad;
 };
 
+// Job groups of one launch, carried in the kernel arguments: a wave finds its group by
+// an unrolled compare chain over g_start (no memory loads).
+constexpr int kMaxGroupsPerLaunch = 32;
+
 struct ConvArgs {
   const float* x;
   const float* w;
   const float* sh;            // harmonics of active edges, compacted within each row
-  const int32_t* row_ptr;     // receiver CSR
+  const int4* node_info;      // per order position: {node, row_ptr[node], active degree, 0}
   const int32_t* act_e;       // active edge ids, compacted within each row (at row_ptr[i] + q)
   const int32_t* act_j;       // their senders
-  const int32_t* deg;         // active edges per row
-  const int32_t* order;       // nodes by active degree, descending
-  const int32_t* task_start;  // prefix of wave tasks per group, from this launch's first group
   float* out;
   const Job* jobs;            // the plan's job table
-  const Group* groups;        // first group of this launch
   int32_t n_nodes;
   int32_t f_in;
   int32_t f_out;
   int32_t w_stride;
   int32_t sh_stride;
-  int32_t n_groups;
-  int32_t total_tasks;
+  int32_t n_groups;           // groups of this launch (<= kMaxGroupsPerLaunch)
   int32_t edge_slots_log2;    // requested edge slots per receiver (clamped per job)
+  int32_t total_tasks;        // wave tasks of this launch
+  int32_t g_start[kMaxGroupsPerLaunch];       // first wave task of each group
+  int32_t g_first_job[kMaxGroupsPerLaunch];
+  int32_t g_n_jobs[kMaxGroupsPerLaunch];
+  int32_t g_lanes_log2[kMaxGroupsPerLaunch];
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -44,6 +44,7 @@ namespace {
 constexpr int kConvThreads = 256;
 constexpr int kConvWaves = kConvThreads / kWave;
 
+
 template <int N>
 struct IntC {
   static constexpr int value = N;
@@ -208,9 +209,10 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int nod
   const bool ok = (node_pos < a.n_nodes) && (ch0 < J.n_ch);
   int i = 0, rb = 0, n_act = 0;
   if (node_pos < a.n_nodes) {
-    i = a.order[node_pos];
-    rb = a.row_ptr[i];
-    n_act = a.deg[i];
+    const int4 ni = a.node_info[node_pos];
+    i = ni.x;
+    rb = ni.y;
+    n_act = ni.z;
   }
   // active edges of row i, compacted within the row: edge ids act_e[rb + q], senders
   // act_j[rb + q], harmonics sh[(rb + q) * sh_stride], q < n_act
@@ -327,20 +329,21 @@ template <int C>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
   const int task = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kConvWaves + int(threadIdx.x) / kWave);
   if (task >= a.total_tasks) return;
-  // task_start holds the prefix over all groups of the plan; this launch starts at ts[0]
-  const int32_t* __restrict__ ts = a.task_start;
-  const int t0 = ts[0];
-  int lo = 0, hi = a.n_groups;  // last group whose first task is <= task
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (ts[mid] - t0 <= task) lo = mid; else hi = mid;
+  // the wave's group: last g with g_start[g] <= task (unrolled, kernel-argument reads)
+  int g_base = 0, g_first = 0, g_nj = 1, lg = 0;
+#pragma unroll
+  for (int g = 0; g < kMaxGroupsPerLaunch; ++g) {
+    if (g < a.n_groups && task >= a.g_start[g]) {
+      g_base = a.g_start[g];
+      g_first = a.g_first_job[g];
+      g_nj = a.g_n_jobs[g];
+      lg = a.g_lanes_log2[g];
+    }
   }
-  const Group G = a.groups[lo];
-  const int r = task - (ts[lo] - t0);
-  const int ng = r / G.n_jobs;                 // node group
-  const Job J = a.jobs[G.first_job + (r - ng * G.n_jobs)];
+  const int r = task - g_base;
+  const int ng = r / g_nj;                     // node group
+  const Job J = a.jobs[g_first + (r - ng * g_nj)];
   const int lane = int(threadIdx.x) & (kWave - 1);
-  const int lg = G.lanes_log2;
   const int sg = min(a.edge_slots_log2, 6 - lg);
   const int node_pos = (ng << (6 - lg - sg)) + (lane >> (lg + sg));
   __shared__ int2 stage[kConvWaves][kStageEntries];

@@ -217,16 +217,16 @@ __global__ void nbr_fill_kernel(const float* __restrict__ pos, int n, GridArgs g
 // One workgroup: act_row_ptr = exclusive scan of deg (if requested); order = node ids
 // sorted by deg descending, ties by id ascending (stable LSD radix sort on
 // maxdeg - deg, 8-bit digits, ranks inside a wave from ballots, across waves from an
-// LDS table); task_start = wave-task prefix of the plan's job groups (if requested).
+// LDS table); node_info[pos] = {node, row_ptr[node], deg[node], 0} of the sorted order
+// (if requested).
 // Degrees are cached in LDS when n <= kDegCache, so each radix pass reads LDS only.
 __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int32_t* __restrict__ deg, int n,
+                                                                      const int32_t* __restrict__ row_ptr,
                                                                       int32_t* __restrict__ act_row_ptr,
                                                                       int32_t* __restrict__ order,
+                                                                      int4* __restrict__ node_info,
                                                                       int32_t* __restrict__ tmp_a,
-                                                                      int32_t* __restrict__ tmp_b,
-                                                                      const Group* __restrict__ groups, int n_groups,
-                                                                      int edge_slots_log2,
-                                                                      int32_t* __restrict__ task_start) {
+                                                                      int32_t* __restrict__ tmp_b) {
   __shared__ int wsum[kScanWaves + 1];
   __shared__ int s_max;
   __shared__ int hist[256];
@@ -239,25 +239,6 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
   const bool cached = n <= kDegCache;
   const int lane = lane_id();
   const int wave = tid / kWave;
-
-  if (task_start) {  // uniform
-    int run = 0;
-    for (int b0 = 0; b0 < n_groups; b0 += kScanThreads) {
-      const int k = b0 + tid;
-      int v = 0;
-      if (k < n_groups) {
-        const int lg = groups[k].lanes_log2;
-        const int sg = edge_slots_log2 < 6 - lg ? edge_slots_log2 : 6 - lg;
-        const int s = 64 >> (lg + sg);  // receivers per wave
-        v = groups[k].n_jobs * ((n + s - 1) / s);
-      }
-      int total;
-      const int ex = block_exclusive_scan(v, wsum, total);
-      if (k < n_groups) task_start[k] = run + ex;
-      run += total;
-    }
-    if (tid == 0) task_start[n_groups] = run;
-  }
 
   // 1. scan (optional) and maximum
   if (tid == 0) s_max = 0;
@@ -284,14 +265,18 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
   int passes = 0;
   for (int m = maxdeg; m > 0; m >>= 8) ++passes;
   if (passes == 0) {
-    for (int idx = tid; idx < n; idx += kScanThreads) order[idx] = idx;
+    for (int idx = tid; idx < n; idx += kScanThreads) {
+      if (order) order[idx] = idx;
+      if (node_info) node_info[idx] = make_int4(idx, row_ptr[idx], 0, 0);
+    }
     return;
   }
 
   const unsigned long long lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
   for (int p = 0; p < passes; ++p) {
     const int32_t* src = (p == 0) ? nullptr : ((p - 1) % 2 == 0 ? tmp_a : tmp_b);
-    int32_t* dst = (p == passes - 1) ? order : (p % 2 == 0 ? tmp_a : tmp_b);
+    const bool last = p == passes - 1;
+    int32_t* dst = last ? order : (p % 2 == 0 ? tmp_a : tmp_b);
     const int shift = 8 * p;
     for (int k = tid; k < 256; k += kScanThreads) hist[k] = 0;
     __syncthreads();
@@ -335,7 +320,11 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
         tile_tot[tid] = run;
       }
       __syncthreads();
-      if (valid) dst[base[digit] + wcnt[wave][digit] + rank] = id;
+      if (valid) {
+        const int at = base[digit] + wcnt[wave][digit] + rank;
+        if (dst) dst[at] = id;
+        if (last && node_info) node_info[at] = make_int4(id, row_ptr[id], cached ? s_deg[id] : deg[id], 0);
+      }
       __syncthreads();
       if (tid < 256) base[tid] += tile_tot[tid];
       __syncthreads();
@@ -559,11 +548,9 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_order(const int32_t* deg, int n, int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
-                        int32_t* tmp_b, const Group* groups, int n_groups, int edge_slots_log2, int32_t* task_start,
-                        hipStream_t s) {
-  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, act_row_ptr, order, tmp_a, tmp_b, groups, n_groups,
-                                                    edge_slots_log2, task_start);
+hipError_t launch_order(const int32_t* deg, int n, const int32_t* row_ptr, int32_t* act_row_ptr, int32_t* order,
+                        int4* node_info, int32_t* tmp_a, int32_t* tmp_b, hipStream_t s) {
+  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, row_ptr, act_row_ptr, order, node_info, tmp_a, tmp_b);
   return hipGetLastError();
 }
 
