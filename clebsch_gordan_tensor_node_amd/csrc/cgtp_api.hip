@@ -141,7 +141,8 @@ struct cgtp_plan_s {
   std::vector<PathInfo> paths;
   int64_t f_in = 0, f_out = 0, w = 0;
   int l_sh_max = 0;
-  int sh_stride = 1;
+  int sh_stride = 1;                 // floats per SH row of cgtp_edge_sh: (l_sh_max + 1)^2
+  int sh_pad = 4;                    // floats per SH row of the forward workspace (multiple of 4)
   std::string irreps_out;
   std::vector<Job> jobs;             // ordered by group
   std::vector<Group> groups;         // by kernel class, heavy groups first
@@ -155,20 +156,22 @@ struct cgtp_plan_s {
 
 namespace {
 
-// Wave-job schedule.  Per path: K = 4 channels per lane when every offset and stride
-// is 16-byte aligned, else K = 1; lanes per node = next power of two of mul/K, at most
-// 64 (larger multiplicities are cut into channel blocks of 64*K).  Jobs are grouped by
-// kernel class and ordered by per-edge cost, heaviest first (LunaTP Table 9: ordering
-// by descending CG-term count was fastest).
+// Job schedule.  Per path: K = 4 channels per lane when every offset and stride is
+// 16-byte aligned, else K = 1; lanes per receiver = next power of two of mul/K, at most
+// 64 (larger multiplicities are cut into channel blocks of 64*K).  Jobs of one kernel
+// class, input irrep, channel block and K form a set that shares x_j rows; each set is
+// cut into groups of at most kConvJobs jobs, one workgroup per group and node group.
+// Jobs are ordered by per-edge cost, heaviest first, inside a set (so a group's waves
+// have similar step times), and groups heaviest first inside a class (LunaTP Table 9:
+// ordering by descending CG-term count was fastest).
 void schedule(cgtp_plan_s& P) {
   P.jobs.clear();
   struct Tmp {
     Job j;
-    int cls;
+    int cls, irrep, block, l2;
     double cost;
   };
   std::vector<Tmp> tmp;
-  std::vector<int> tmp_irrep, tmp_block;
   std::vector<int> used(kNumVariants, 0);
   const bool strides4 = (P.f_in % 4 == 0) && (P.f_out % 4 == 0) && (P.w % 4 == 0);
   int plan_lmax = 0;
@@ -178,6 +181,7 @@ void schedule(cgtp_plan_s& P) {
     const bool al = strides4 && p.mul % 4 == 0 && p.in_off % 4 == 0 && p.out_off % 4 == 0 && p.w_off % 4 == 0;
     const int K = al ? 4 : 1;
     const int v = variant_index(p.l1, p.l2, p.l3, K);
+    const int cls = job_class(v, plan_lmax);
     used[v] = 1;
     std::vector<float> cg;
     dense_cg(p.l1, p.l2, p.l3, cg);
@@ -197,7 +201,6 @@ void schedule(cgtp_plan_s& P) {
     const int block = 64 * K;
     for (int c0 = 0; c0 < p.mul; c0 += block) {
       const int n_ch = std::min(block, p.mul - c0);
-      // lanes per receiver; the remaining lane bits select the receiver of the wave
       const int lanes = next_pow2((n_ch + K - 1) / K);
       Job j{};
       j.variant = v;
@@ -208,77 +211,74 @@ void schedule(cgtp_plan_s& P) {
       j.w_off = p.w_off + c0;
       j.sh_off = p.l2 * p.l2;
       j.path = int(pi);
-      tmp.push_back(Tmp{j, job_class(v, plan_lmax), cost});
-      tmp_irrep.push_back(p.i_in);
-      tmp_block.push_back(c0);
+      tmp.push_back(Tmp{j, cls, p.i_in, c0, p.l2, cost});
     }
   }
-  // groups: (class, input irrep, channel block); heavy groups first inside a class,
-  // heavy jobs first inside a group
-  struct Key {
-    int cls, irrep, block;
-    bool operator<(const Key& o) const {
-      if (cls != o.cls) return cls < o.cls;
-      if (irrep != o.irrep) return irrep < o.irrep;
-      return block < o.block;
-    }
-    bool operator==(const Key& o) const { return cls == o.cls && irrep == o.irrep && block == o.block; }
+  // sets of jobs sharing (class, input irrep, channel block, K)
+  auto key_less = [&](const Tmp& x, const Tmp& y) {
+    if (x.cls != y.cls) return x.cls < y.cls;
+    if (x.irrep != y.irrep) return x.irrep < y.irrep;
+    if (x.block != y.block) return x.block < y.block;
+    const int kx = variant_desc(x.j.variant).k, ky = variant_desc(y.j.variant).k;
+    if (kx != ky) return kx < ky;
+    return x.cost > y.cost;   // heavy jobs first inside a set
   };
-  std::vector<Key> keys;
-  for (size_t k = 0; k < tmp.size(); ++k) keys.push_back(Key{tmp[k].cls, tmp_irrep[k], tmp_block[k]});
-  std::vector<Key> uniq = keys;
-  std::sort(uniq.begin(), uniq.end());
-  uniq.erase(std::unique(uniq.begin(), uniq.end()), uniq.end());
-  std::vector<double> gcost(uniq.size(), 0.0);
-  std::vector<int> gid(tmp.size());
-  for (size_t k = 0; k < tmp.size(); ++k) {
-    gid[k] = int(std::lower_bound(uniq.begin(), uniq.end(), keys[k]) - uniq.begin());
-    gcost[gid[k]] += tmp[k].cost;
+  std::stable_sort(tmp.begin(), tmp.end(), key_less);
+  struct G {
+    int cls, begin, n;
+    double cost;
+  };
+  std::vector<G> gs;
+  for (size_t b = 0; b < tmp.size();) {
+    size_t e = b + 1;
+    while (e < tmp.size() && tmp[b].cls == tmp[e].cls && tmp[b].irrep == tmp[e].irrep &&
+           tmp[b].block == tmp[e].block && variant_desc(tmp[b].j.variant).k == variant_desc(tmp[e].j.variant).k)
+      ++e;
+    // cut the set [b, e) into ceil(n / kConvJobs) groups of balanced size
+    const int n = int(e - b), ng = (n + kConvJobs - 1) / kConvJobs;
+    int at = int(b);
+    for (int g = 0; g < ng; ++g) {
+      const int sz = n / ng + (g < n % ng ? 1 : 0);
+      gs.push_back(G{tmp[b].cls, at, sz, tmp[at].cost});
+      at += sz;
+    }
+    b = e;
   }
-  std::vector<int> gorder(uniq.size());
-  for (size_t g = 0; g < uniq.size(); ++g) gorder[g] = int(g);
-  std::stable_sort(gorder.begin(), gorder.end(), [&](int a, int b) {
-    if (uniq[a].cls != uniq[b].cls) return uniq[a].cls < uniq[b].cls;
-    return gcost[a] > gcost[b];
+  std::stable_sort(gs.begin(), gs.end(), [](const G& x, const G& y) {
+    if (x.cls != y.cls) return x.cls < y.cls;
+    return x.cost > y.cost;
   });
   P.groups.clear();
   P.class_begin.assign(kNumClasses + 1, 0);
-  for (int g : gorder) {
-    std::vector<int> members;
-    for (size_t k = 0; k < tmp.size(); ++k)
-      if (gid[k] == g) members.push_back(int(k));
-    std::stable_sort(members.begin(), members.end(), [&](int a, int b) { return tmp[a].cost > tmp[b].cost; });
+  for (const G& g : gs) {
     Group G{};
     G.first_job = int(P.jobs.size());
-    G.n_jobs = int(members.size());
-    G.lanes_log2 = tmp[members[0]].j.lanes_log2;
-    for (int k : members) P.jobs.push_back(tmp[k].j);
+    G.n_jobs = g.n;
+    G.lanes_log2 = tmp[g.begin].j.lanes_log2;
+    int l2lo = kMaxL, l2hi = 0;
+    for (int k = g.begin; k < g.begin + g.n; ++k) {
+      P.jobs.push_back(tmp[k].j);
+      l2lo = std::min(l2lo, tmp[k].l2);
+      l2hi = std::max(l2hi, tmp[k].l2);
+    }
+    G.y0 = (l2lo * l2lo) / 4 * 4;
+    G.y4 = ((l2hi + 1) * (l2hi + 1) - G.y0 + 3) / 4;
+    // at least y4 lanes per receiver, so that the S y4 harmonic chunks of a step fit the
+    // producer wave's 64 lanes (extra lanes idle)
+    G.lanes_log2 = std::max(G.lanes_log2, ilog2(next_pow2(G.y4)));
+    for (int k = G.first_job; k < G.first_job + G.n_jobs; ++k) P.jobs[k].lanes_log2 = G.lanes_log2;
     P.groups.push_back(G);
-    P.class_begin[uniq[g].cls + 1]++;
+    P.class_begin[g.cls + 1]++;
   }
   for (int c = 0; c < kNumClasses; ++c) P.class_begin[c + 1] += P.class_begin[c];
   P.n_variants = 0;
   for (int u : used) P.n_variants += u;
 }
 
-int64_t tasks_of(const Group& g, int64_t n, int edge_slots_log2) {
-  const int sg = std::min(edge_slots_log2, 6 - g.lanes_log2);
-  const int s = 64 >> (g.lanes_log2 + sg);  // receivers per wave
-  return int64_t(g.n_jobs) * ((n + s - 1) / s);
-}
-
-// Edge slots per receiver for this graph size: only when one receiver per lane group
-// would leave SIMDs without a wave (small graphs) are a receiver's edges split over
-// edge slots; each extra wave pays a prologue of dependent loads, which measured
-// slower than a longer edge loop whenever the grid already fills the GPU.
-constexpr int64_t kTargetWaves = 256 * 4;
-int choose_edge_slots_log2(const cgtp_plan_s& P, int64_t n) {
-  for (int sg = 0; sg < 3; ++sg) {
-    int64_t waves = 0;
-    for (const Group& g : P.groups) waves += tasks_of(g, n, sg);
-    if (waves >= kTargetWaves) return sg;
-  }
-  return 3;
+// workgroups of a group: one per node group of 64 / 2^lanes_log2 receivers
+int64_t tasks_of(const Group& g, int64_t n) {
+  const int s = 64 >> g.lanes_log2;
+  return (n + s - 1) / s;
 }
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -309,7 +309,7 @@ FwdWorkspace carve(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
   w.tmp_b = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.act_e = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.act_j = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
-  w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_stride) * 4));
+  w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_pad) * 4));
   w.bytes = off;
   return w;
 }
@@ -416,6 +416,7 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   P->l_sh_max = 0;
   for (const Irrep& r : P->sh) P->l_sh_max = std::max(P->l_sh_max, r.l);
   P->sh_stride = (P->l_sh_max + 1) * (P->l_sh_max + 1);
+  P->sh_pad = (P->sh_stride + 3) / 4 * 4;
   P->irreps_out = format_irreps(P->out);
   schedule(*P);
 
@@ -637,15 +638,15 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   g.act_e = ws.act_e;
   g.act_j = ws.act_j;
   g.sh = ws.sh;
+  g.sh_stride = P->sh_pad;
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
   CGTP_HIP(launch_rows(g, P->l_sh_max, s));
   // 2. node order by active degree (LunaTP Table 9), as position-indexed node records
-  const int sg = choose_edge_slots_log2(*P, n_nodes);
   CGTP_HIP(launch_order(ws.deg, int(n_nodes), row_ptr, nullptr, nullptr, ws.node_info, ws.tmp_a, ws.tmp_b, s));
   // 3. the fused convolution: per kernel class, launches of up to kMaxGroupsPerLaunch
-  //    job groups whose task ranges travel in the kernel arguments
+  //    job groups whose workgroup ranges travel in the kernel arguments
   ConvArgs a{};
   a.x = x;
   a.w = w;
@@ -659,8 +660,7 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   a.f_in = int(P->f_in);
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
-  a.sh_stride = P->sh_stride;
-  a.edge_slots_log2 = sg;
+  a.sh_stride = P->sh_pad;
   struct Launch {
     int cls, g0, g1;
   };
@@ -670,18 +670,20 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
       launches.push_back(Launch{c, g0, std::min(P->class_begin[c + 1], g0 + kMaxGroupsPerLaunch)});
   for (size_t li = 0; li < launches.size(); ++li) {
     const Launch& L = launches[li];
-    int64_t tasks = 0;
+    int64_t wgs = 0;
     a.n_groups = L.g1 - L.g0;
     for (int k = L.g0; k < L.g1; ++k) {
       const Group& G = P->groups[k];
-      a.g_start[k - L.g0] = int(tasks);
+      a.g_start[k - L.g0] = int(wgs);
       a.g_first_job[k - L.g0] = G.first_job;
       a.g_n_jobs[k - L.g0] = G.n_jobs;
       a.g_lanes_log2[k - L.g0] = G.lanes_log2;
-      tasks += tasks_of(G, n_nodes, sg);
+      a.g_y0[k - L.g0] = G.y0;
+      a.g_y4[k - L.g0] = G.y4;
+      wgs += tasks_of(G, n_nodes);
     }
-    if (tasks > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many wave tasks");
-    a.total_tasks = int(tasks);
+    if (wgs > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
+    a.total_wgs = int(wgs);
     CGTP_HIP(launch_conv(a, L.cls, s, li == 0 ? ev_begin : nullptr, li + 1 == launches.size() ? ev_end : nullptr));
   }
   const int first_cls = launches.empty() ? -1 : launches.front().cls;

@@ -12,10 +12,10 @@ namespace cgtp {
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxShL = kMaxL;       // harmonics up to l = 6
 
-// One wave job: a path p and a block of its channels.  A wave runs one job for
-// S = 64 / 2^lanes_log2 consecutive receivers of the degree-sorted order; 2^lanes_log2
-// lanes serve one receiver, each lane owning K consecutive channels.  (LunaTP Figure
-// 3(b): paths mapped to SIMD lanes by channel block; sized to the 64-lane wavefront.)
+// One wave job: a path p and a block of its channels.  2^lanes_log2 lanes serve one
+// receiver, each lane owning K consecutive channels, so one wave covers
+// S = 64 / 2^lanes_log2 receivers of the degree-sorted order.  (LunaTP Figure 3(b):
+// paths mapped to SIMD lanes by channel block; sized to the 64-lane wavefront.)
 struct Job {
   int32_t variant;     // index of the (l1, l2, l3, K) specialisation
   int32_t lanes_log2;  // log2 of the lanes serving one receiver (<= 64)
@@ -28,19 +28,22 @@ struct Job {
 };
 static_assert(sizeof(Job) == 32, "Job is 32 bytes");
 
-// A group: the jobs of one input irrep, one channel block and one kernel class.  They
-// read the same columns of x and use the same lanes per receiver, so their tasks are
-// interleaved (node group major, job minor): the waves of one workgroup then run
-// different paths on the same receivers and share the gathered x_j rows in the CU's L1
-// cache (LunaTP Table 8: cross-path input reuse).
+// A group: up to kConvJobs jobs of one input irrep, one channel block, one K and one
+// kernel class, run by one workgroup per node group: one consumer wave per job and one
+// producer wave.  The jobs read the same x_j rows and the same harmonics, which the
+// producer gathers once per edge step into LDS (LunaTP Table 8: cross-path input reuse);
+// each consumer streams only its own path's weights.
+constexpr int kConvWaves = 4;
+constexpr int kConvJobs = kConvWaves - 1;
 struct Group {
   int32_t first_job;   // index into the plan's job table
-  int32_t n_jobs;
-  int32_t lanes_log2;
-  int32_t pad;
+  int32_t n_jobs;      // 1 .. kConvJobs
+  int32_t lanes_log2;  // lanes per receiver, common to the jobs
+  int32_t y0;          // first harmonic (float offset in an SH row, multiple of 4) staged
+  int32_t y4;          // 16-byte chunks of harmonics staged per receiver
 };
 
-// Job groups of one launch, carried in the kernel arguments: a wave finds its group by
+// Groups of one launch, carried in the kernel arguments: a workgroup finds its group by
 // an unrolled compare chain over g_start (no memory loads).
 constexpr int kMaxGroupsPerLaunch = 32;
 
@@ -57,14 +60,15 @@ struct ConvArgs {
   int32_t f_in;
   int32_t f_out;
   int32_t w_stride;
-  int32_t sh_stride;
+  int32_t sh_stride;          // floats per SH row (a multiple of 4)
   int32_t n_groups;           // groups of this launch (<= kMaxGroupsPerLaunch)
-  int32_t edge_slots_log2;    // requested edge slots per receiver (clamped per job)
-  int32_t total_tasks;        // wave tasks of this launch
-  int32_t g_start[kMaxGroupsPerLaunch];       // first wave task of each group
+  int32_t total_wgs;          // workgroups of this launch
+  int32_t g_start[kMaxGroupsPerLaunch];       // first workgroup of each group
   int32_t g_first_job[kMaxGroupsPerLaunch];
   int32_t g_n_jobs[kMaxGroupsPerLaunch];
   int32_t g_lanes_log2[kMaxGroupsPerLaunch];
+  int32_t g_y0[kMaxGroupsPerLaunch];
+  int32_t g_y4[kMaxGroupsPerLaunch];
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

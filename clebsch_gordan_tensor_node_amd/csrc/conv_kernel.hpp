@@ -3,25 +3,26 @@
 // LunaTP ("Enabling Efficient and Scalable Tensor Product for Equivariant MLIPs")
 // Figure 3: (a) node-centric execution sums the messages of all incoming edges on chip
 // and stores each output once; (b) paths are grouped and mapped to SIMD lanes by
-// channel block; (c) products are reused and equal coefficients factored.  This is
-// the gfx950 design, not a translation:
-//   * a wave (64 lanes) runs one job = (path, channel block) for Sn consecutive
-//     receivers of the degree-sorted node order (LunaTP Table 9: descending degree
-//     first); each receiver gets Se edge slots of T lanes (Sn Se T = 64), each lane
-//     owning K channels; the edge slots split the receiver's edges round robin and are
-//     summed by a butterfly at the end, so long rows do not set the kernel's tail;
+// channel block; (c) products are reused and equal coefficients factored; Table 8:
+// inputs shared across paths.  This is the gfx950 design, not a translation:
+//   * a workgroup of 4 waves serves one group (up to 4 paths of one input irrep and
+//     channel block) on S consecutive receivers of the degree-sorted order (LunaTP
+//     Table 9: descending degree first); wave p runs path p with T = 64 / S lanes per
+//     receiver, each lane owning K channels;
+//   * the receivers' active edges are walked in lock step, one edge per receiver per
+//     step.  Per step the workgroup gathers the senders' x_j segments and the edges'
+//     harmonics once, each thread one 16-byte share, into a double-buffered LDS stage;
+//     one barrier publishes it and every wave reads its operands from LDS.  The only
+//     per-path stream is the lane's own K weights of the edge;
+//   * loads run D steps ahead of use in a register ring that holds only the thread's
+//     shares and weights, so the pipeline is deep for few VGPRs; the edge and sender
+//     indices of the receivers are staged in LDS first, so no index load waits behind
+//     data loads in the wave's in-order memory counter;
 //   * the path is a compile-time specialisation: the real CG coefficients and their
 //     sparsity are constants, so A[m1,m3] = sum_m2 C[m1,m2,m3] Y[m2] is a short FMA
-//     chain with immediate coefficients and structural zeros removed;
-//   * per edge a lane loads its K weights (one 16-byte load when K = 4), its K x_j
-//     channel vectors and the edge's Y_l2, forms A once, and applies it to its K
-//     channels: acc[k,m3] += w[k] * sum_m1 A[m1,m3] x[k,m1], scaling whichever side
+//     chain with immediate coefficients and structural zeros removed, applied to the K
+//     channels as acc[k,m3] += w[k] * sum_m1 A[m1,m3] x[k,m1], scaling whichever side
 //     (x or the partial result) is shorter;
-//   * the edge loop is a software pipeline: the operands of the next D-1 edges are in
-//     flight (a ring of register buffers) while one edge is accumulated; the edge and
-//     sender indices of the receivers are staged in a wave-private LDS area first, so
-//     no index load waits behind data loads in the in-order memory counter and no
-//     register that a load is still filling is ever copied;
 //   * accumulators live in VGPRs for the whole edge loop; one coalesced store per
 //     receiver and channel block at the end.  No atomics: the result is bitwise
 //     reproducible.
@@ -41,9 +42,8 @@ namespace cgtp {
 
 namespace {
 
-constexpr int kConvThreads = 256;
-constexpr int kConvWaves = kConvThreads / kWave;
-
+constexpr int kConvThreads = kConvWaves * kWave;
+constexpr int kStageLog2 = 10;   // (edge, sender) pairs staged per workgroup and window
 
 template <int N>
 struct IntC {
@@ -172,190 +172,311 @@ __device__ __forceinline__ void accumulate_edge(float* acc, float* xv, const flo
   }
 }
 
-template <int K, int N1, int N2>
-struct EdgeBuf {
-  float x[K * N1];
-  float w[K];
-  float y[N2];
+// LDS of one workgroup of class C (sized by the class's largest l1).  Per step the
+// producer wave stores N1 x chunks and one harmonic chunk per lane; chunk c of a step
+// sits at c * (chunk floats), so the stage is receiver-major.  Chunks past the step's
+// data land in the padding.
+template <int C>
+struct ConvSmem {
+  static constexpr int kN1 = 2 * class_max_l1(C) + 1;
+  float x[2][kWave * kN1 * 4];      // x_j segments of one step (double-buffered)
+  float y[2][kWave * 4];            // harmonics of one step (double-buffered)
+  uint32_t sx[1 << kStageLog2];     // staged j f_in (x element offset of the sender's row)
+  uint32_t sw[1 << kStageLog2];     // staged (e - row start) W (w offset from the receiver's rows)
+  uint32_t sy[1 << kStageLog2];     // staged q sh_stride (SH offset from the receiver's rows)
+  int4 slot[kWave];                 // receiver records {node or -1, row start, active degree, 0}
 };
 
-// Ring depth: edges whose operands are in flight while one edge is accumulated.
-template <int N1>
-constexpr int ring_depth() {
-  return N1 <= 5 ? 3 : 2;
+// Pipeline depths (edge steps whose loads are in flight while one step is used).  The
+// producer's loads (x_j rows, harmonics) mostly hit the L2 cache and need few steps;
+// the consumers' weight loads come from HBM once and get a deep ring of K floats a slot.
+template <int N1, int K>
+constexpr int producer_depth() {
+  return N1 * K + 4 <= 16 ? 3 : 2;
+}
+template <int K>
+constexpr int consumer_depth() {
+  return K == 4 ? 8 : 12;
 }
 
-// Wave-private LDS staging of edge indices: kStageEntries (edge, sender) pairs per
-// wave, shared by its receivers (kStageEntries / Sn each).
-constexpr int kStageEntries = 512;
+__device__ __forceinline__ const float* byte_off(const float* base, uint32_t bytes) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + bytes);
+}
 
-// Lane layout of a wave: lane = (node slot, edge slot, channel lane) with T = 2^lg
-// channel lanes, Se = 2^sg edge slots and Sn = 64 / (T Se) node slots.  Edge slot es
-// of a receiver takes its active edges es, es + Se, ...; the edge slots are summed by a
-// butterfly at the end.
-template <int L1, int L2, int L3, int K>
-__device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int node_pos, int lane, int lg, int sg,
-                                        int2* __restrict__ stage) {
+// One wave of a workgroup.  Waves 0 .. kConvJobs-1 are consumers, one job each (or idle
+// when the group has fewer jobs); wave kConvJobs is the producer.  Consumer lane layout:
+// lane = (receiver slot ns, channel lane t) with T = 2^lg channel lanes and S = 64 / T
+// receivers (node positions ng S .. ng S + S - 1).  Stage layout per step: receiver r's
+// x_j segment (n_ch N1 floats) at r n_ch N1, cut into chunks of K floats, chunk c loaded
+// by producer lane c mod 64; receiver r's harmonics Y[y0 .. y0 + 4 y4) at r 4 y4 (the
+// schedule keeps S y4 <= 64: one 16-byte chunk per producer lane).
+//
+// Steps past a receiver's last active edge repeat that edge (its offsets are staged
+// again) with the weight replaced by zero, so every load is of real, finite data; a
+// receiver without active edges stores zeros.  Every load of a pipeline step is issued
+// unconditionally: a skipped load would make the wave's in-order memory counter
+// ambiguous and force full waits.
+template <int C, int L1, int L2, int L3, int K>
+__device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng, int lg, int y0, int y4, int wave,
+                                        bool has_job, ConvSmem<C>& sm) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  constexpr int D = ring_depth<N1>();
-  const int T = 1 << lg;
-  const int Se = 1 << sg;
-  const int t = lane & (T - 1);
-  const int es = (lane >> lg) & (Se - 1);
-  const int nslot = lane >> (lg + sg);
-  const int cap = kStageEntries >> (6 - lg - sg);   // staged edges per receiver and window
-  int2* __restrict__ my_stage = stage + nslot * cap;
-  const int ch0 = t * K;
-  const bool ok = (node_pos < a.n_nodes) && (ch0 < J.n_ch);
-  int i = 0, rb = 0, n_act = 0;
-  if (node_pos < a.n_nodes) {
-    const int4 ni = a.node_info[node_pos];
-    i = ni.x;
-    rb = ni.y;
-    n_act = ni.z;
+  static_assert(N1 <= ConvSmem<C>::kN1, "x stage too small for this variant");
+  const int tid = int(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int S = kWave >> lg;
+  const int n_ch = J.n_ch;
+  const int cap_log2 = kStageLog2 - (6 - lg);       // staged entries per receiver and window
+
+  if (tid < S) {
+    const int pos = ng * S + tid;
+    sm.slot[tid] = pos < a.n_nodes ? a.node_info[pos] : make_int4(-1, 0, 0, 0);
   }
-  // active edges of row i, compacted within the row: edge ids act_e[rb + q], senders
-  // act_j[rb + q], harmonics sh[(rb + q) * sh_stride], q < n_act
-  int qmax = n_act;
+  __syncthreads();
+  // the node order is by active degree, descending: the first receiver has the most edges
+  const int qmax = __builtin_amdgcn_readfirstlane(sm.slot[0].z);
+
+  // stage the element offsets of every (receiver, step) of a window; a step past the
+  // receiver's last edge repeats that edge, a receiver with no edge uses zeros
+  auto stage = [&](int qw, int steps) {
+    const int spl = steps > 1 ? 32 - __clz(steps - 1) : 0;
+    for (int idx = tid; idx < (S << spl); idx += kConvThreads) {
+      const int r = idx >> spl, k = idx & ((1 << spl) - 1);
+      if (k < steps) {
+        const int4 si = sm.slot[r];
+        uint32_t ox = 0, ow = 0, oy = 0;
+        if (si.z > 0) {
+          const int q = min(qw + k, si.z - 1);
+          const int e = a.act_e[si.y + q];
+          const int j = a.act_j[si.y + q];
+          ox = uint32_t(j) * uint32_t(a.f_in);
+          ow = uint32_t(e - si.y) * uint32_t(a.w_stride);
+          oy = uint32_t(q) * uint32_t(a.sh_stride);
+        }
+        const int at = (r << cap_log2) + k;
+        sm.sx[at] = ox;
+        sm.sw[at] = ow;
+        sm.sy[at] = oy;
+      }
+    }
+  };
+
+  if (wave == kConvJobs) {
+    // ---------------- producer: x_j segments and harmonics of every step ----------------
+    constexpr int D = producer_depth<N1, K>();
+    const int cps = n_ch * N1 / K;                  // x chunks per receiver
+    uint32_t x_off[N1];
+    int x_sl[N1];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) qmax = max(qmax, __shfl_xor(qmax, off, kWave));
-  qmax = __builtin_amdgcn_readfirstlane(qmax);
+    for (int i = 0; i < N1; ++i) {
+      const int c = lane + kWave * i;
+      x_sl[i] = 0;
+      x_off[i] = uint32_t(J.in_off);
+      if (c < S * cps) {
+        const int r = c / cps;
+        x_sl[i] = r << cap_log2;
+        x_off[i] = uint32_t(J.in_off + (c - r * cps) * K);
+      }
+    }
+    int y_sl = 0;
+    const float* ybase = a.sh + y0;
+    if (lane < S * y4) {
+      const int r = lane / y4;
+      const int4 si = sm.slot[r];
+      y_sl = r << cap_log2;
+      ybase = a.sh + (long)(si.z > 0 ? si.y : 0) * a.sh_stride + y0 + 4 * (lane - r * y4);
+    }
+    struct PSlot {
+      float x[N1 * K];
+      float y[4];
+    };
+    struct PIdx {
+      uint32_t x[N1];
+      uint32_t y;
+    };
+    PSlot ring[D];
+    for (int qw = 0; qw < qmax; qw += (1 << cap_log2)) {
+      const int steps = min(1 << cap_log2, qmax - qw);
+      stage(qw, steps);
+      __syncthreads();
+      auto fetch = [&](int k, PIdx& ix) {
+        const int kk = min(k, steps - 1);
+#pragma unroll
+        for (int i = 0; i < N1; ++i) ix.x[i] = (sm.sx[x_sl[i] + kk] + x_off[i]) * 4u;
+        ix.y = sm.sy[y_sl + kk] * 4u;
+      };
+      auto issue = [&](const PIdx& ix, PSlot& b) {
+#pragma unroll
+        for (int i = 0; i < N1; ++i) load_k<K>(byte_off(a.x, ix.x[i]), b.x + i * K);
+        const float4 v = *reinterpret_cast<const float4*>(byte_off(ybase, ix.y));
+        b.y[0] = v.x;
+        b.y[1] = v.y;
+        b.y[2] = v.z;
+        b.y[3] = v.w;
+        // keep the steps' loads in program order: the memory counter is in order, and a
+        // step's loads scheduled after a later step's would make that step wait for both
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto publish = [&](int k, PSlot& b) {
+        float* xs = sm.x[k & 1];
+#pragma unroll
+        for (int i = 0; i < N1; ++i) store_run<K, K>(xs + (lane + kWave * i) * K, b.x + i * K);
+        store_run<4, 4>(sm.y[k & 1] + lane * 4, b.y);
+        __syncthreads();
+      };
+      // every step issues its loads unconditionally (past the window's end they repeat
+      // its last step), so the wave's memory counter is exact on every path; only the
+      // publishing, which holds no load, is skipped past the end
+      PIdx ix;
+      static_for<0, D - 1>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        fetch(p, ix);
+        issue(ix, ring[p]);
+      });
+      fetch(D - 1, ix);
+      for (int k0 = 0; k0 < steps; k0 += D) {
+        static_for<0, D>([&](auto Sx) {
+          constexpr int s = decltype(Sx)::value;
+          issue(ix, ring[(s + D - 1) % D]);
+          fetch(k0 + s + D, ix);
+          if (k0 + s < steps) publish(k0 + s, ring[s]);
+        });
+      }
+      __syncthreads();   // every staged offset and stage buffer consumed before re-staging
+    }
+    return;
+  }
+
+  if (!has_job) {
+    // ---------------- idle consumer: keep the workgroup's barrier count ----------------
+    for (int qw = 0; qw < qmax; qw += (1 << cap_log2)) {
+      const int steps = min(1 << cap_log2, qmax - qw);
+      stage(qw, steps);
+      __syncthreads();
+      for (int k = 0; k < steps; ++k) __syncthreads();
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- consumer: this job's weights and accumulation ----------------
+  constexpr int D = consumer_depth<K>();
+  const int t = lane & ((1 << lg) - 1);
+  const int ns = lane >> lg;
+  const int ch0 = t * K;
+  const int4 my = sm.slot[ns];
+  const int w_n = ch0 < n_ch ? my.z : 0;
+  const int w_sl = ns << cap_log2;
+  const float* __restrict__ wbase =
+      a.w + (long)(my.z > 0 ? my.y : 0) * a.w_stride + J.w_off + (ch0 < n_ch ? ch0 : 0);
+  const int x_rd = (ns * n_ch + ch0) * N1;          // this lane's operands in the x stage
+  const int y_rd = ns * 4 * y4 + J.sh_off - y0;     // ... and its Y_l2 in the harmonic stage
 
   float acc[K * N3];
 #pragma unroll
   for (int q = 0; q < K * N3; ++q) acc[q] = 0.0f;
-
-  const float* __restrict__ xb = a.x + J.in_off + ch0 * N1;
-  const float* __restrict__ wb = a.w + J.w_off + ch0;
-  const float* __restrict__ shb = a.sh + J.sh_off + (long)rb * a.sh_stride;
-  const int32_t* __restrict__ ae = a.act_e + rb;
-  const int32_t* __restrict__ aj = a.act_j + rb;
-
-  // Ring buffers start at zero; a lane with no edge at some step accumulates with a zero
-  // weight, so the accumulate step has no branch and the compiler can track every
-  // buffer's outstanding loads exactly.
-  EdgeBuf<K, N1, N2> ring[D];
+  float ring[D][K];
+  for (int qw = 0; qw < qmax; qw += (1 << cap_log2)) {
+    const int steps = min(1 << cap_log2, qmax - qw);
+    stage(qw, steps);
+    __syncthreads();
+    auto fetch = [&](int k) { return sm.sw[w_sl + min(k, steps - 1)] * 4u; };
+    auto issue = [&](uint32_t ow, float* b) {
+      load_k<K>(byte_off(wbase, ow), b);
+      __builtin_amdgcn_sched_barrier(0);   // loads stay in step order (see the producer)
+    };
+    auto use = [&](int k, float* b) {
+      __syncthreads();   // the producer has published step k
+      // the weights are first touched here, after the barrier: without this the
+      // scheduler hoists the selects of all unrolled steps above the loop's barriers and
+      // waits for every weight load at once
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
+      for (int m = 0; m < K; ++m) asm volatile("" : "+v"(b[m]));
+      const bool live = qw + k < w_n;
+      float wv[K];
 #pragma unroll
-    for (int m = 0; m < K * N1; ++m) ring[d].x[m] = 0.0f;
+      for (int m = 0; m < K; ++m) wv[m] = live ? b[m] : 0.0f;
+      float xv[K * N1];
+      load_run<K, K * N1>(sm.x[k & 1] + x_rd, xv);
+      float Y[N2];
+      const float* ys = sm.y[k & 1] + y_rd;
 #pragma unroll
-    for (int m = 0; m < K; ++m) ring[d].w[m] = 0.0f;
-#pragma unroll
-    for (int m = 0; m < N2; ++m) ring[d].y[m] = 0.0f;
-  }
-  // step k of a window: this lane's edge is q = qw + k Se + es
-  auto issue = [&](int k, int qw, EdgeBuf<K, N1, N2>& b) {
-    const int q = qw + (k << sg) + es;
-    if (ok && q < n_act) {
-      const int2 ej = my_stage[q - qw];
-      load_run<K, K * N1>(xb + (long)ej.y * a.f_in, b.x);
-      load_k<K>(wb + (long)ej.x * a.w_stride, b.w);
-      const float* ys = shb + (long)q * a.sh_stride;
-#pragma unroll
-      for (int m = 0; m < N2; ++m) b.y[m] = ys[m];
-    }
-  };
-  auto consume = [&](int k, int qw, EdgeBuf<K, N1, N2>& b) {
-    const bool live = ok && (qw + (k << sg) + es) < n_act;
-    float wv[K];
-#pragma unroll
-    for (int m = 0; m < K; ++m) wv[m] = live ? b.w[m] : 0.0f;
-    accumulate_edge<L1, L2, L3, K>(acc, b.x, wv, b.y);
-  };
-
-  for (int qw = 0; qw < qmax; qw += cap) {   // windows of `cap` edges (one for short rows)
-    const int qend = min(qmax, qw + cap);
-    const int steps = (qend - qw + Se - 1) >> sg;
-    // stage this window's indices: the receiver's lanes copy them cooperatively; LDS
-    // operations of one wave complete in order, so the fences only order the compiler
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    for (int q = qw + (lane & (T * Se - 1)); q < min(n_act, qend); q += T * Se)
-      my_stage[q - qw] = make_int2(ae[q], aj[q]);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // software pipeline: the operands of the next D-1 edges are in flight while one
-    // edge is accumulated; ring slots are static after unrolling by D
+      for (int m = 0; m < N2; ++m) Y[m] = ys[m];
+      accumulate_edge<L1, L2, L3, K>(acc, xv, wv, Y);
+    };
+    // as in the producer: loads unconditional, only the use skipped past the end
     static_for<0, D - 1>([&](auto P) {
       constexpr int p = decltype(P)::value;
-      if (p < steps) issue(p, qw, ring[p]);
+      issue(fetch(p), ring[p]);
     });
-    int k0 = 0;
-    for (; k0 + 2 * D - 2 < steps; k0 += D) {   // steady state: every step issues
+    uint32_t ow = fetch(D - 1);
+    for (int k0 = 0; k0 < steps; k0 += D) {
       static_for<0, D>([&](auto Sx) {
         constexpr int s = decltype(Sx)::value;
-        issue(k0 + s + D - 1, qw, ring[(s + D - 1) % D]);
-        consume(k0 + s, qw, ring[s]);
+        issue(ow, ring[(s + D - 1) % D]);
+        ow = fetch(k0 + s + D);
+        if (k0 + s < steps) use(k0 + s, ring[s]);
       });
     }
-    for (; k0 < steps; k0 += D) {               // drain
-      static_for<0, D>([&](auto Sx) {
-        constexpr int s = decltype(Sx)::value;
-        const int k = k0 + s;
-        if (k < steps) {
-          if (k + D - 1 < steps) issue(k + D - 1, qw, ring[(s + D - 1) % D]);
-          consume(k, qw, ring[s]);
-        }
-      });
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");  // staged entries consumed
+    __syncthreads();
   }
-  // sum the edge slots of each receiver (lane bits lg .. lg+sg-1); slot 0 stores
-  for (int off = T; off < (T << sg); off <<= 1) {
+  if (ch0 < n_ch && my.x >= 0) {
+    if (my.z == 0) {
 #pragma unroll
-    for (int q = 0; q < K * N3; ++q) acc[q] += __shfl_xor(acc[q], off, kWave);
+      for (int q = 0; q < K * N3; ++q) acc[q] = 0.0f;
+    }
+    store_run<K, K * N3>(a.out + (long)my.x * a.f_out + J.out_off + ch0 * N3, acc);
   }
-  if (ok && es == 0) store_run<K, K * N3>(a.out + (long)i * a.f_out + J.out_off + ch0 * N3, acc);
 }
 
 template <int C, int LO, int HI>
-__device__ __forceinline__ void dispatch(int v, const ConvArgs& a, const Job& J, int node_pos, int lane, int lg,
-                                         int sg, int2* stage) {
+__device__ __forceinline__ void dispatch(int v, const ConvArgs& a, const Job& J, int ng, int lg, int y0, int y4,
+                                         int wave, bool has_job, ConvSmem<C>& sm) {
   if constexpr (HI - LO == 1) {
     if constexpr (class_contains(C, LO)) {
       constexpr VariantDesc d = variant_desc(LO);
-      run_job<d.l1, d.l2, d.l3, d.k>(a, J, node_pos, lane, lg, sg, stage);
+      run_job<C, d.l1, d.l2, d.l3, d.k>(a, J, ng, lg, y0, y4, wave, has_job, sm);
     }
   } else {
     constexpr int MID = (LO + HI) / 2;
     if (v < MID)
-      dispatch<C, LO, MID>(v, a, J, node_pos, lane, lg, sg, stage);
+      dispatch<C, LO, MID>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
     else
-      dispatch<C, MID, HI>(v, a, J, node_pos, lane, lg, sg, stage);
+      dispatch<C, MID, HI>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
   }
 }
 
+// One workgroup per (group, node group): the producer wave and one consumer wave per job
+// (consumer waves past the group's job count only keep the barrier count).  The producer
+// runs the first job's code path, which fixes l1, K and the channel block it gathers.
 template <int C>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
-  const int task = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kConvWaves + int(threadIdx.x) / kWave);
-  if (task >= a.total_tasks) return;
-  // the wave's group: last g with g_start[g] <= task (unrolled, kernel-argument reads)
-  int g_base = 0, g_first = 0, g_nj = 1, lg = 0;
+  const int wg = int(blockIdx.x);
+  // the workgroup's group: last g with g_start[g] <= wg (unrolled, kernel-argument reads)
+  int g_base = 0, g_first = 0, g_nj = 1, lg = 0, y0 = 0, y4 = 1;
 #pragma unroll
   for (int g = 0; g < kMaxGroupsPerLaunch; ++g) {
-    if (g < a.n_groups && task >= a.g_start[g]) {
+    if (g < a.n_groups && wg >= a.g_start[g]) {
       g_base = a.g_start[g];
       g_first = a.g_first_job[g];
       g_nj = a.g_n_jobs[g];
       lg = a.g_lanes_log2[g];
+      y0 = a.g_y0[g];
+      y4 = a.g_y4[g];
     }
   }
-  const int r = task - g_base;
-  const int ng = r / g_nj;                     // node group
-  const Job J = a.jobs[g_first + (r - ng * g_nj)];
-  const int lane = int(threadIdx.x) & (kWave - 1);
-  const int sg = min(a.edge_slots_log2, 6 - lg);
-  const int node_pos = (ng << (6 - lg - sg)) + (lane >> (lg + sg));
-  __shared__ int2 stage[kConvWaves][kStageEntries];
-  dispatch<C, 0, kNumVariants>(J.variant, a, J, node_pos, lane, lg, sg, stage[threadIdx.x / kWave]);
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+  const bool has_job = wave < g_nj;
+  const Job J = a.jobs[g_first + (has_job ? wave : 0)];
+  __shared__ ConvSmem<C> sm;
+  dispatch<C, 0, kNumVariants>(J.variant, a, J, wg - g_base, lg, y0, y4, wave, has_job, sm);
 }
 
 }  // namespace
 
 template <int C>
 hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (args.total_tasks <= 0) return hipSuccess;
-  const int blocks = ceil_div(args.total_tasks, kConvWaves);
+  if (args.total_wgs <= 0) return hipSuccess;
+  const int blocks = args.total_wgs;
   if (ev_start || ev_stop) {
     // the events are stamped by the dispatch itself: kernel time without launch gaps
     hipExtLaunchKernelGGL(conv_kernel<C>, dim3(blocks), dim3(kConvThreads), 0, s, ev_start, ev_stop, 0, args);

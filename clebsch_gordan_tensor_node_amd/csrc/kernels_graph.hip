@@ -401,6 +401,7 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
     float* out = a.sh + (long)slot * a.sh_stride;
 #pragma unroll
     for (int q = 0; q < NY; ++q) out[q] = float(Y[q]);
+    for (int q = NY; q < a.sh_stride; ++q) out[q] = 0.0f;
   }
   if (a.deg && lane == 0) a.deg[row] = cnt;
 }
@@ -532,7 +533,7 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
   a.sh = p.sh;
   a.n_nodes = p.n_nodes;
   a.has_cell = p.has_cell;
-  a.sh_stride = (l_sh_max + 1) * (l_sh_max + 1);
+  a.sh_stride = p.sh_stride > 0 ? p.sh_stride : (l_sh_max + 1) * (l_sh_max + 1);
   for (int k = 0; k < 9; ++k) a.cell[k] = p.cell[k];
   const int nb = ceil_div(p.n_nodes, kRowThreads / kWave);
   switch (l_sh_max) {

@@ -48,6 +48,7 @@ struct RowPass {
   int32_t* act_e;  // active edge ids compacted within each row (at row_ptr[i] + q)
   int32_t* act_j;  // their senders
   float* sh;       // their harmonics, same slots
+  int sh_stride;   // floats per SH row (0: (l_sh_max + 1)^2); entries past (l_sh_max + 1)^2 are zeroed
   int n_nodes;
   int n_edges;
   int has_cell;
@@ -66,8 +67,9 @@ hipError_t launch_order(const int32_t* deg, int n, const int32_t* row_ptr, int32
 hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int32_t* act_row_ptr, int n_nodes,
                           int n_edges, int32_t* act_eid, hipStream_t s);
 
-// The fused conv kernel of one variant class over `args.total_tasks` wave tasks
-// (one explicit instantiation per class, each in its own translation unit).
+// The fused conv kernel of one variant class over `args.total_wgs` workgroups (one per
+// job group and node group; one explicit instantiation per class, each in its own
+// translation unit).
 // ev_start / ev_stop (may be null): HIP events stamped at this launch's start / end.
 template <int C>
 hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);

@@ -69,6 +69,8 @@ constexpr bool class_contains(int c, int v) {
   if (c == 1) return m <= 3;
   return m >= 4 && variant_desc(v).l1 == c - 2;
 }
+// Largest l1 among the variants of class c (it sizes the class's LDS staging).
+constexpr int class_max_l1(int c) { return c == 0 ? 2 : c == 1 ? 3 : c - 2; }
 // class of a variant inside a plan whose largest l is plan_lmax
 constexpr int job_class(int v, int plan_lmax) {
   const int m = variant_lmax(v);
