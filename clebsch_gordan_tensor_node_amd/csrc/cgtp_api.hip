@@ -161,9 +161,9 @@ namespace {
 // 64 (larger multiplicities are cut into channel blocks of 64*K).  Jobs of one kernel
 // class, input irrep, channel block and K form a set that shares x_j rows; each set is
 // cut into groups of at most kConvJobs jobs, one workgroup per group and node group.
-// Jobs are ordered by per-edge cost, heaviest first, inside a set (so a group's waves
-// have similar step times), and groups heaviest first inside a class (LunaTP Table 9:
-// ordering by descending CG-term count was fastest).
+// Jobs keep their weight-column order inside a set, so that a group's consumers read
+// adjacent columns of each weight row; groups are ordered heaviest first inside a class
+// (LunaTP Table 9: ordering by descending CG-term count was fastest).
 void schedule(cgtp_plan_s& P) {
   P.jobs.clear();
   struct Tmp {
@@ -221,7 +221,7 @@ void schedule(cgtp_plan_s& P) {
     if (x.block != y.block) return x.block < y.block;
     const int kx = variant_desc(x.j.variant).k, ky = variant_desc(y.j.variant).k;
     if (kx != ky) return kx < ky;
-    return x.cost > y.cost;   // heavy jobs first inside a set
+    return x.j.w_off < y.j.w_off;   // weight-column order inside a set
   };
   std::stable_sort(tmp.begin(), tmp.end(), key_less);
   struct G {
@@ -239,7 +239,9 @@ void schedule(cgtp_plan_s& P) {
     int at = int(b);
     for (int g = 0; g < ng; ++g) {
       const int sz = n / ng + (g < n % ng ? 1 : 0);
-      gs.push_back(G{tmp[b].cls, at, sz, tmp[at].cost});
+      double c = 0.0;
+      for (int k = at; k < at + sz; ++k) c = std::max(c, tmp[k].cost);
+      gs.push_back(G{tmp[b].cls, at, sz, c});
       at += sz;
     }
     b = e;
@@ -275,11 +277,6 @@ void schedule(cgtp_plan_s& P) {
   for (int u : used) P.n_variants += u;
 }
 
-// workgroups of a group: one per node group of 64 / 2^lanes_log2 receivers
-int64_t tasks_of(const Group& g, int64_t n) {
-  const int s = 64 >> g.lanes_log2;
-  return (n + s - 1) / s;
-}
 
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
@@ -668,21 +665,30 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   for (int c = 0; c < kNumClasses; ++c)
     for (int g0 = P->class_begin[c]; g0 < P->class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
       launches.push_back(Launch{c, g0, std::min(P->class_begin[c + 1], g0 + kMaxGroupsPerLaunch)});
+  // Workgroups are dispatched block by block: a block of B = 64 / 2^lg_min receivers
+  // (the largest node group of the launch) holds B / S_g node groups of every group g, so
+  // the groups of one block, which read the same weight rows, run at the same time.
   for (size_t li = 0; li < launches.size(); ++li) {
     const Launch& L = launches[li];
-    int64_t wgs = 0;
     a.n_groups = L.g1 - L.g0;
+    int lg_min = 6;
+    for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, P->groups[k].lanes_log2);
+    int per_block = 0;
     for (int k = L.g0; k < L.g1; ++k) {
       const Group& G = P->groups[k];
-      a.g_start[k - L.g0] = int(wgs);
+      a.g_start[k - L.g0] = per_block;
       a.g_first_job[k - L.g0] = G.first_job;
       a.g_n_jobs[k - L.g0] = G.n_jobs;
       a.g_lanes_log2[k - L.g0] = G.lanes_log2;
       a.g_y0[k - L.g0] = G.y0;
       a.g_y4[k - L.g0] = G.y4;
-      wgs += tasks_of(G, n_nodes);
+      per_block += 1 << (G.lanes_log2 - lg_min);
     }
+    const int64_t block = 64 >> lg_min;
+    const int64_t wgs = (n_nodes + block - 1) / block * per_block;
     if (wgs > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
+    a.blk_wgs = per_block;
+    a.blk_lg_min = lg_min;
     a.total_wgs = int(wgs);
     CGTP_HIP(launch_conv(a, L.cls, s, li == 0 ? ev_begin : nullptr, li + 1 == launches.size() ? ev_end : nullptr));
   }

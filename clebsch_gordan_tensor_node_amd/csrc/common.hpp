@@ -43,8 +43,10 @@ struct Group {
   int32_t y4;          // 16-byte chunks of harmonics staged per receiver
 };
 
-// Groups of one launch, carried in the kernel arguments: a workgroup finds its group by
-// an unrolled compare chain over g_start (no memory loads).
+// Groups of one launch, carried in the kernel arguments.  Workgroups come in blocks of
+// 64 / 2^blk_lg_min consecutive receivers of the degree order; a block holds
+// 2^(lanes_log2 - blk_lg_min) workgroups of each group, and a workgroup finds its group
+// by an unrolled compare chain over g_start (no memory loads).
 constexpr int kMaxGroupsPerLaunch = 32;
 
 struct ConvArgs {
@@ -62,8 +64,10 @@ struct ConvArgs {
   int32_t w_stride;
   int32_t sh_stride;          // floats per SH row (a multiple of 4)
   int32_t n_groups;           // groups of this launch (<= kMaxGroupsPerLaunch)
-  int32_t total_wgs;          // workgroups of this launch
-  int32_t g_start[kMaxGroupsPerLaunch];       // first workgroup of each group
+  int32_t total_wgs;          // workgroups of this launch (whole blocks)
+  int32_t blk_wgs;            // workgroups per block of 64 / 2^blk_lg_min receivers
+  int32_t blk_lg_min;         // smallest lanes_log2 of the launch's groups
+  int32_t g_start[kMaxGroupsPerLaunch];       // first workgroup of each group inside a block
   int32_t g_first_job[kMaxGroupsPerLaunch];
   int32_t g_n_jobs[kMaxGroupsPerLaunch];
   int32_t g_lanes_log2[kMaxGroupsPerLaunch];

@@ -94,6 +94,23 @@ __device__ __forceinline__ void load_k(const float* __restrict__ p, float* v) {
   }
 }
 
+// K floats read once (the weights): a non-temporal load, so that the stream does not
+// evict the x rows and harmonics that the producer gathers again and again from L2
+template <int K>
+__device__ __forceinline__ void load_k_stream(const float* __restrict__ p, float* v) {
+  if constexpr (K == 4) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 q = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+    v[0] = q[0];
+    v[1] = q[1];
+    v[2] = q[2];
+    v[3] = q[3];
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = __builtin_nontemporal_load(p + k);
+  }
+}
+
 // n contiguous floats, n a multiple of 4 when K == 4 (16-byte aligned source)
 template <int K, int N>
 __device__ __forceinline__ void load_run(const float* __restrict__ p, float* v) {
@@ -181,9 +198,11 @@ struct ConvSmem {
   static constexpr int kN1 = 2 * class_max_l1(C) + 1;
   float x[2][kWave * kN1 * 4];      // x_j segments of one step (double-buffered)
   float y[2][kWave * 4];            // harmonics of one step (double-buffered)
-  uint32_t sx[1 << kStageLog2];     // staged j f_in (x element offset of the sender's row)
-  uint32_t sw[1 << kStageLog2];     // staged (e - row start) W (w offset from the receiver's rows)
-  uint32_t sy[1 << kStageLog2];     // staged q sh_stride (SH offset from the receiver's rows)
+  // staged offsets, receiver r's window at r (cap + 1): the odd row stride puts the
+  // receivers of one read on different LDS banks
+  uint32_t sx[(1 << kStageLog2) + kWave];   // j f_in (x element offset of the sender's row)
+  uint32_t sw[(1 << kStageLog2) + kWave];   // (e - row start) W (w offset from the receiver's rows)
+  uint32_t sy[(1 << kStageLog2) + kWave];   // q sh_stride (SH offset from the receiver's rows)
   int4 slot[kWave];                 // receiver records {node or -1, row start, active degree, 0}
 };
 
@@ -192,7 +211,8 @@ struct ConvSmem {
 // the consumers' weight loads come from HBM once and get a deep ring of K floats a slot.
 template <int N1, int K>
 constexpr int producer_depth() {
-  return N1 * K + 4 <= 16 ? 3 : 2;
+  constexpr int d = 72 / (N1 * K + 4);
+  return d < 2 ? 2 : (d > 4 ? 4 : d);
 }
 template <int K>
 constexpr int consumer_depth() {
@@ -226,6 +246,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
   const int S = kWave >> lg;
   const int n_ch = J.n_ch;
   const int cap_log2 = kStageLog2 - (6 - lg);       // staged entries per receiver and window
+  const int srow = (1 << cap_log2) + 1;             // stage row stride
 
   if (tid < S) {
     const int pos = ng * S + tid;
@@ -252,7 +273,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
           ow = uint32_t(e - si.y) * uint32_t(a.w_stride);
           oy = uint32_t(q) * uint32_t(a.sh_stride);
         }
-        const int at = (r << cap_log2) + k;
+        const int at = r * srow + k;
         sm.sx[at] = ox;
         sm.sw[at] = ow;
         sm.sy[at] = oy;
@@ -273,7 +294,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
       x_off[i] = uint32_t(J.in_off);
       if (c < S * cps) {
         const int r = c / cps;
-        x_sl[i] = r << cap_log2;
+        x_sl[i] = r * srow;
         x_off[i] = uint32_t(J.in_off + (c - r * cps) * K);
       }
     }
@@ -282,7 +303,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
     if (lane < S * y4) {
       const int r = lane / y4;
       const int4 si = sm.slot[r];
-      y_sl = r << cap_log2;
+      y_sl = r * srow;
       ybase = a.sh + (long)(si.z > 0 ? si.y : 0) * a.sh_stride + y0 + 4 * (lane - r * y4);
     }
     struct PSlot {
@@ -365,7 +386,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
   const int ch0 = t * K;
   const int4 my = sm.slot[ns];
   const int w_n = ch0 < n_ch ? my.z : 0;
-  const int w_sl = ns << cap_log2;
+  const int w_sl = ns * srow;
   const float* __restrict__ wbase =
       a.w + (long)(my.z > 0 ? my.y : 0) * a.w_stride + J.w_off + (ch0 < n_ch ? ch0 : 0);
   const int x_rd = (ns * n_ch + ch0) * N1;          // this lane's operands in the x stage
@@ -381,7 +402,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
     __syncthreads();
     auto fetch = [&](int k) { return sm.sw[w_sl + min(k, steps - 1)] * 4u; };
     auto issue = [&](uint32_t ow, float* b) {
-      load_k<K>(byte_off(wbase, ow), b);
+      load_k_stream<K>(byte_off(wbase, ow), b);
       __builtin_amdgcn_sched_barrier(0);   // loads stay in step order (see the producer)
     };
     auto use = [&](int k, float* b) {
@@ -450,7 +471,8 @@ __device__ __forceinline__ void dispatch(int v, const ConvArgs& a, const Job& J,
 // runs the first job's code path, which fixes l1, K and the channel block it gathers.
 template <int C>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
-  const int wg = int(blockIdx.x);
+  const int blk = int(blockIdx.x) / a.blk_wgs;
+  const int wg = int(blockIdx.x) - blk * a.blk_wgs;
   // the workgroup's group: last g with g_start[g] <= wg (unrolled, kernel-argument reads)
   int g_base = 0, g_first = 0, g_nj = 1, lg = 0, y0 = 0, y4 = 1;
 #pragma unroll
@@ -468,7 +490,8 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
   const bool has_job = wave < g_nj;
   const Job J = a.jobs[g_first + (has_job ? wave : 0)];
   __shared__ ConvSmem<C> sm;
-  dispatch<C, 0, kNumVariants>(J.variant, a, J, wg - g_base, lg, y0, y4, wave, has_job, sm);
+  const int ng = (blk << (lg - a.blk_lg_min)) + (wg - g_base);   // node group of this group
+  dispatch<C, 0, kNumVariants>(J.variant, a, J, ng, lg, y0, y4, wave, has_job, sm);
 }
 
 }  // namespace
