@@ -579,7 +579,7 @@ int cgtp_conv_prepare(cgtp_plan_t P, const int32_t* row_ptr, const uint8_t* mask
   rp.n_nodes = int(n_nodes);
   rp.n_edges = int(n_edges);
   CGTP_HIP(launch_rows(rp, P->l_sh_max, s));
-  CGTP_HIP(launch_order(w.deg, int(n_nodes), row_ptr, act_row_ptr, order, nullptr, w.tmp_a, w.tmp_b, s));
+  CGTP_HIP(launch_order(w.deg, int(n_nodes), act_row_ptr, order, w.tmp_a, w.tmp_b, s));
   CGTP_HIP(launch_compact(row_ptr, mask, act_row_ptr, int(n_nodes), int(n_edges), act_eid, s));
   return ok();
 }
@@ -641,7 +641,7 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   fill_cell(g, cell);
   CGTP_HIP(launch_rows(g, P->l_sh_max, s));
   // 2. node order by active degree (LunaTP Table 9), as position-indexed node records
-  CGTP_HIP(launch_order(ws.deg, int(n_nodes), row_ptr, nullptr, nullptr, ws.node_info, ws.tmp_a, ws.tmp_b, s));
+  CGTP_HIP(launch_degree_order(ws.deg, int(n_nodes), row_ptr, ws.node_info, s));
   // 3. the fused convolution: per kernel class, launches of up to kMaxGroupsPerLaunch
   //    job groups whose workgroup ranges travel in the kernel arguments
   ConvArgs a{};

@@ -217,14 +217,11 @@ __global__ void nbr_fill_kernel(const float* __restrict__ pos, int n, GridArgs g
 // One workgroup: act_row_ptr = exclusive scan of deg (if requested); order = node ids
 // sorted by deg descending, ties by id ascending (stable LSD radix sort on
 // maxdeg - deg, 8-bit digits, ranks inside a wave from ballots, across waves from an
-// LDS table); node_info[pos] = {node, row_ptr[node], deg[node], 0} of the sorted order
-// (if requested).
+// LDS table).
 // Degrees are cached in LDS when n <= kDegCache, so each radix pass reads LDS only.
 __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int32_t* __restrict__ deg, int n,
-                                                                      const int32_t* __restrict__ row_ptr,
                                                                       int32_t* __restrict__ act_row_ptr,
                                                                       int32_t* __restrict__ order,
-                                                                      int4* __restrict__ node_info,
                                                                       int32_t* __restrict__ tmp_a,
                                                                       int32_t* __restrict__ tmp_b) {
   __shared__ int wsum[kScanWaves + 1];
@@ -265,10 +262,8 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
   int passes = 0;
   for (int m = maxdeg; m > 0; m >>= 8) ++passes;
   if (passes == 0) {
-    for (int idx = tid; idx < n; idx += kScanThreads) {
+    for (int idx = tid; idx < n; idx += kScanThreads)
       if (order) order[idx] = idx;
-      if (node_info) node_info[idx] = make_int4(idx, row_ptr[idx], 0, 0);
-    }
     return;
   }
 
@@ -323,12 +318,46 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
       if (valid) {
         const int at = base[digit] + wcnt[wave][digit] + rank;
         if (dst) dst[at] = id;
-        if (last && node_info) node_info[at] = make_int4(id, row_ptr[id], cached ? s_deg[id] : deg[id], 0);
       }
       __syncthreads();
       if (tid < 256) base[tid] += tile_tot[tid];
       __syncthreads();
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Node records of the forward: node_info[pos] = {node, row_ptr[node], deg[node], 0} in
+// descending degree order (LunaTP Table 9), as a one-pass counting sort in one
+// workgroup: LDS histogram of the degrees, scan from the largest degree down, and each
+// node placed by an LDS atomic on its degree's cursor.  Nodes of equal degree land in
+// any order (the convolution of a receiver does not depend on its position); degrees
+// above kOrderBins - 1 share the top bin.
+// ---------------------------------------------------------------------------------
+
+constexpr int kOrderBins = kScanThreads;
+
+__global__ void __launch_bounds__(kScanThreads) degree_order_kernel(const int32_t* __restrict__ deg, int n,
+                                                                    const int32_t* __restrict__ row_ptr,
+                                                                    int4* __restrict__ node_info) {
+  __shared__ int wsum[kScanWaves + 1];
+  __shared__ int cursor[kOrderBins];
+  const int tid = threadIdx.x;
+  cursor[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kScanThreads) atomicAdd(&cursor[min(deg[i], kOrderBins - 1)], 1);
+  __syncthreads();
+  // exclusive scan over the bins from the top degree down
+  const int b = kOrderBins - 1 - tid;
+  const int cnt = cursor[b];
+  int total;
+  const int ex = block_exclusive_scan(cnt, wsum, total);
+  cursor[b] = ex;
+  __syncthreads();
+  for (int i = tid; i < n; i += kScanThreads) {
+    const int d = deg[i];
+    const int pos = atomicAdd(&cursor[min(d, kOrderBins - 1)], 1);
+    node_info[pos] = make_int4(i, row_ptr[i], d, 0);
   }
 }
 
@@ -549,9 +578,15 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_order(const int32_t* deg, int n, const int32_t* row_ptr, int32_t* act_row_ptr, int32_t* order,
-                        int4* node_info, int32_t* tmp_a, int32_t* tmp_b, hipStream_t s) {
-  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, row_ptr, act_row_ptr, order, node_info, tmp_a, tmp_b);
+hipError_t launch_order(const int32_t* deg, int n, int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
+                        int32_t* tmp_b, hipStream_t s) {
+  prep_scan_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, act_row_ptr, order, tmp_a, tmp_b);
+  return hipGetLastError();
+}
+
+hipError_t launch_degree_order(const int32_t* deg, int n, const int32_t* row_ptr, int4* node_info, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  degree_order_kernel<<<1, kScanThreads, 0, s>>>(deg, n, row_ptr, node_info);
   return hipGetLastError();
 }
 

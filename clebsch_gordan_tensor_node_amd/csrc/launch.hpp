@@ -56,12 +56,15 @@ struct RowPass {
 };
 hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s);
 
-// One workgroup: optional exclusive scan of deg into act_row_ptr, node order by deg
-// descending (ties by id) into order (may be null), and the position-indexed record
-// node_info[pos] = {node, row_ptr[node], deg[node], 0} (may be null).
+// One workgroup: optional exclusive scan of deg into act_row_ptr and the node order by
+// deg descending, ties by id ascending, into order (may be null).
 // tmp_a, tmp_b: [n] int32 scratch.
-hipError_t launch_order(const int32_t* deg, int n, const int32_t* row_ptr, int32_t* act_row_ptr, int32_t* order,
-                        int4* node_info, int32_t* tmp_a, int32_t* tmp_b, hipStream_t s);
+hipError_t launch_order(const int32_t* deg, int n, int32_t* act_row_ptr, int32_t* order, int32_t* tmp_a,
+                        int32_t* tmp_b, hipStream_t s);
+
+// node_info[pos] = {node, row_ptr[node], deg[node], 0} by descending degree; nodes of
+// equal degree in any order (one workgroup).
+hipError_t launch_degree_order(const int32_t* deg, int n, const int32_t* row_ptr, int4* node_info, hipStream_t s);
 
 // Ids of the active edges in CSR order, at act_row_ptr[i] + rank within row i.
 hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int32_t* act_row_ptr, int n_nodes,
