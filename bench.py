@@ -197,10 +197,12 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         ms_warm = t_beg.elapsed_time(t_end) / K
 
-    # algorithmic bytes of one conv launch: weights of active edges, their compacted ids,
-    # senders and harmonics, node features in, outputs out, per-node row pointers/order
-    conv_bytes = (4 * plan.w_per_edge * e_act + e_act * (8 + 4 * plan.sh_stride)
-                  + 4 * plan.f_in * n + 4 * plan.f_out * n + 12 * n)
+    # algorithmic bytes of the hot path, each moved once: the weights of the active edges
+    # (4 W per active edge), the edge list (4 col + 3 shift, + 1 mask byte when masked,
+    # per edge), the row pointers (4 (N + 1)), 12 bytes of positions per node, and the
+    # node features in and the outputs out (4 F_in and 4 F_out per node)
+    conv_bytes = (4 * plan.w_per_edge * e_act + e * (4 + 3 + (1 if mask is not None else 0))
+                  + 4 * (n + 1) + 12 * n + 4 * plan.f_in * n + 4 * plan.f_out * n)
     achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
     traffic = read_traffic(wl.name)
 

@@ -617,6 +617,8 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   if (n_edges > 0 && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(col, 4))
     return fail(CGTP_ERR_INVALID_ARG, "x, w and out must be 16-byte aligned");
+  if (double(n_nodes) * double(P->f_in) * 4.0 >= 4294967296.0)
+    return fail(CGTP_ERR_UNSUPPORTED, "x is 4 GiB or larger (32-bit byte offsets)");
   const FwdWorkspace ws = carve(*P, n_nodes, n_edges, workspace);
   if (!workspace || ws_bytes < ws.bytes)
     return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, ws.bytes);

@@ -143,7 +143,9 @@ int cgtp_edge_sh(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const floa
 /* The CGTP convolution forward.  out[n_nodes, f_out] is overwritten (not accumulated);
  * rows with no active edge get exactly 0; w and x_j of inactive edges are never read.
  * Arguments as above; x [n_nodes, f_in], w [n_edges, w_per_edge], mask NULL = all
- * active.  All device pointers 16-byte aligned.  Asynchronous on `stream`. */
+ * active.  All device pointers 16-byte aligned; x must be smaller than 4 GiB (the
+ * kernel addresses it with 32-bit byte offsets), else CGTP_ERR_UNSUPPORTED.
+ * Asynchronous on `stream`.  The result is bitwise reproducible from run to run. */
 int cgtp_conv_forward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
                       const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
                       int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
