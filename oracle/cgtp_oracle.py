@@ -423,13 +423,28 @@ def edge_sh(plan: Plan, r: np.ndarray) -> np.ndarray:
     return np.concatenate([real_sh(l, r) for _, l, _ in plan.irreps_sh], axis=1)
 
 
-def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None) -> np.ndarray:
-    """out [N, F_out] fp64.  Inactive edges (mask == 0) are never read: their w and
-    x_j cannot reach the output even when they hold NaN.  Rows with no active edge
-    are exactly 0."""
+def _active_mask(mask, gate, n_edges):
+    """BranchIP sparse evaluation (Method): an edge is active when the mask (if any) keeps
+    it and its continuation gate (if any) is not exactly zero."""
+    if mask is None and gate is None:
+        return None
+    act = np.ones(n_edges, dtype=bool)
+    if mask is not None:
+        act &= np.asarray(mask) != 0
+    if gate is not None:
+        act &= np.asarray(gate, dtype=np.float64) != 0.0
+    return act.astype(np.uint8)
+
+
+def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, gate=None) -> np.ndarray:
+    """out [N, F_out] fp64.  Inactive edges (mask == 0, or gate == 0) are never read:
+    their w and x_j cannot reach the output even when they hold NaN.  Rows with no
+    active edge are exactly 0.  gate [E] (optional): BranchIP's continuation gate, which
+    multiplies each edge's feature before the tensor product (BranchIP, Method); the
+    product is linear in that feature, so the edge's message is scaled by gate[e]."""
     row_ptr = np.asarray(row_ptr, dtype=np.int64)
     n = row_ptr.shape[0] - 1
-    act_row_ptr, act_eid, _ = prepare(row_ptr, mask)
+    act_row_ptr, act_eid, _ = prepare(row_ptr, _active_mask(mask, gate, len(col)))
     act_row_ptr = act_row_ptr.astype(np.int64)
     ids = act_eid.astype(np.int64)
     out = np.zeros((n, plan.f_out))
@@ -449,12 +464,14 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None) ->
         A = np.einsum("abc,eb->eac", C, Y[p.l2])          # [E_act, n1, n3]
         msg = np.matmul(xj, A)                            # [E_act, mul, n3]
         msg *= wf[ids, p.w_off:p.w_off + p.mul][:, :, None]
+        if gate is not None:
+            msg *= np.asarray(gate, dtype=np.float64)[ids][:, None, None]
         summed = np.add.reduceat(msg, starts, axis=0)     # one sum per receiver
         out[recv_rows, p.out_off:p.out_off + p.mul * n3] += summed.reshape(len(recv_rows), -1)
     return out
 
 
-def conv_forward_loops(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None) -> np.ndarray:
+def conv_forward_loops(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, gate=None) -> np.ndarray:
     """The same definition as pure-Python loops over receiver, edge, path, channel,
     m1, m2, m3 (for tiny inputs only): the brute-force cross-check of conv_forward."""
     row_ptr = [int(v) for v in row_ptr]
@@ -464,6 +481,9 @@ def conv_forward_loops(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=No
     for i in range(n):
         for e in range(row_ptr[i], row_ptr[i + 1]):
             if mask is not None and mask[e] == 0:
+                continue
+            g = 1.0 if gate is None else float(gate[e])
+            if g == 0.0:
                 continue
             j = int(col[e])
             r = [float(pos[j][k]) - float(pos[i][k]) for k in range(3)]
@@ -481,7 +501,7 @@ def conv_forward_loops(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=No
                             xv = float(x[j][p.in_off + u * (2 * p.l1 + 1) + m1])
                             for m2 in range(2 * p.l2 + 1):
                                 acc += C[m1, m2, m3] * xv * Y[m2]
-                        out[i, p.out_off + u * (2 * p.l3 + 1) + m3] += wv * acc
+                        out[i, p.out_off + u * (2 * p.l3 + 1) + m3] += g * wv * acc
     return out
 
 

@@ -234,3 +234,49 @@ def test_sparse_equals_dense_and_nan_never_read():
     # all edges masked: exactly zero
     z = O.conv_forward(plan, pos, cell, rp, col, sh, x, w, np.zeros_like(mask))
     assert np.all(z == 0.0)
+
+
+def _gate(rng, e):
+    """A continuation gate with a flat exact-zero region: half the edges exactly 0, the
+    rest in (0, 1] (BranchIP, Method)."""
+    g = rng.random(e)
+    return np.where(rng.random(e) < 0.5, 0.0, 1.0 - g)
+
+
+def test_gate_equals_dense_with_scaled_weights():
+    # gating an edge's feature scales its message: the gated sparse evaluation equals the
+    # ungated dense one with each weight row multiplied by the gate (zero rows included)
+    plan, pos, box, cell, rp, col, sh, x, w, _ = _case(*CASES["si"])
+    g = _gate(np.random.default_rng(3), len(col))
+    gated = O.conv_forward(plan, pos, cell, rp, col, sh, x, w, gate=g)
+    dense = O.conv_forward(plan, pos, cell, rp, col, sh, x, w * g[:, None])
+    np.testing.assert_allclose(gated, dense, rtol=0, atol=1e-13 * np.abs(dense).max())
+
+
+def test_gate_special_cases_and_nan_never_read():
+    plan, pos, box, cell, rp, col, sh, x, w, mask = _case(*CASES["case2"], masked=True)
+    e = len(col)
+    plain = O.conv_forward(plan, pos, cell, rp, col, sh, x, w)
+    # a gate of ones is no gate; a 0/1 gate is the mask
+    np.testing.assert_array_equal(O.conv_forward(plan, pos, cell, rp, col, sh, x, w, gate=np.ones(e)), plain)
+    np.testing.assert_array_equal(
+        O.conv_forward(plan, pos, cell, rp, col, sh, x, w, gate=mask.astype(np.float64)),
+        O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask))
+    # a constant gate scales the whole output
+    np.testing.assert_allclose(O.conv_forward(plan, pos, cell, rp, col, sh, x, w, gate=np.full(e, 0.25)),
+                               0.25 * plain, rtol=0, atol=1e-14 * np.abs(plain).max())
+    # zero-gated edges are never read, also combined with a mask
+    g = _gate(np.random.default_rng(5), e)
+    ref = O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask, g)
+    wn = w.copy()
+    wn[(g == 0) | (mask == 0)] = np.nan
+    np.testing.assert_array_equal(O.conv_forward(plan, pos, cell, rp, col, sh, x, wn, mask, g), ref)
+
+
+def test_gated_vectorised_equals_python_loops():
+    plan, pos, box, cell, rp, col, sh, x, w, mask = _case(*CASES["tiny"], n=16, box_len=5.0, cutoff=2.6,
+                                                          masked=True)
+    g = _gate(np.random.default_rng(7), len(col))
+    a = O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask, g)
+    b = O.conv_forward_loops(plan, pos, cell, rp, col, sh, x, w, mask, g)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
