@@ -75,11 +75,12 @@ def cpu_baseline(wl, min_seconds: float):
     rp, col, sh = O.neighbors(pos, box, wl.cutoff)
     plan = O.build_plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
     x, w, mask = WL.draw_payload(wl, rng, wl.n_atoms, plan.f_in, len(col), plan.w_per_edge)
+    gate = WL.gate_values(wl, rng, len(col))
     reps, spent = 0, 0.0
     with threadpool_limits(1):
         while reps == 0 or (spent < min_seconds and reps < 20):
             t0 = time.perf_counter()
-            O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask)
+            O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask, gate)
             spent += time.perf_counter() - t0
             reps += 1
     return {"value": len(col) * reps / spent, "unit": "edges/s", "cores": 1, "kind": "oracle",
@@ -144,7 +145,14 @@ def main(argv=None) -> int:
 
     plan = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
     x, w, mask = WL.draw_payload(wl, rng, n, plan.f_in, e, plan.w_per_edge)
-    e_act = int(mask.sum()) if mask is not None else e
+    gate = WL.gate_values(wl, rng, e)
+    active = np.ones(e, dtype=bool)
+    if mask is not None:
+        active &= mask != 0
+    if gate is not None:
+        active &= gate != 0
+    e_act = int(active.sum())
+    gate_d = torch.from_numpy(gate).to(dev) if gate is not None else None
     x_d = torch.from_numpy(x).to(dev)
     mask_d = torch.from_numpy(mask).to(dev) if mask is not None else None
     w_bytes = w.nbytes
@@ -156,7 +164,7 @@ def main(argv=None) -> int:
 
     def step(s, evs=None):
         C.conv_forward(plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs[s % k], mask_d, out=outs[s % k],
-                       workspace=ws, conv_events=evs)
+                       workspace=ws, conv_events=evs, gate=gate_d)
 
     K, W = a.steps, a.warmup
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -192,16 +200,18 @@ def main(argv=None) -> int:
         t_beg.record()
         for s in range(K):
             C.conv_forward(plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs[0], mask_d, out=outs[0],
-                           workspace=ws)
+                           workspace=ws, gate=gate_d)
         t_end.record()
         torch.cuda.synchronize()
         ms_warm = t_beg.elapsed_time(t_end) / K
 
     # algorithmic bytes of the hot path, each moved once: the weights of the active edges
     # (4 W per active edge), the edge list (4 col + 3 shift, + 1 mask byte when masked,
-    # per edge), the row pointers (4 (N + 1)), 12 bytes of positions per node, and the
-    # node features in and the outputs out (4 F_in and 4 F_out per node)
-    conv_bytes = (4 * plan.w_per_edge * e_act + e * (4 + 3 + (1 if mask is not None else 0))
+    # + 4 gate bytes when gated, per edge), the row pointers (4 (N + 1)), 12 bytes of
+    # positions per node, and the node features in and the outputs out (4 F_in and
+    # 4 F_out per node)
+    conv_bytes = (4 * plan.w_per_edge * e_act
+                  + e * (4 + 3 + (1 if mask is not None else 0) + (4 if gate is not None else 0))
                   + 4 * (n + 1) + 12 * n + 4 * plan.f_in * n + 4 * plan.f_out * n)
     achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
     traffic = read_traffic(wl.name)
@@ -221,7 +231,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "n_atoms": n, "n_edges": e, "n_active_edges": e_act,
                    "cutoff": wl.cutoff, "irreps_in": wl.irreps_in, "irreps_sh": wl.irreps_sh,
-                   "irreps_out": plan.irreps_out, "paths": plan.n_paths, "masked": wl.masked,
+                   "irreps_out": plan.irreps_out, "paths": plan.n_paths, "masked": wl.masked, "gated": wl.gated,
                    "description": wl.description},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

@@ -200,9 +200,11 @@ def edge_sh(plan: Plan, pos, cell, row_ptr, col, shift):
 
 
 def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, out=None, workspace=None,
-                 conv_events=None):
+                 conv_events=None, gate=None):
     """out[N, f_out] of the CGTP convolution (asynchronous on the current stream).
 
+    gate: optional fp32 [E] continuation gate (BranchIP): zero-gated edges are inactive,
+    the others' messages are scaled by the gate.
     conv_events: optional (begin, end) torch.cuda.Event pair (each recorded once before,
     so that its HIP event exists); the library records them around the fused
     convolution kernel launches."""
@@ -218,16 +220,18 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, ou
     _dev(w, torch.float32, "w", (e, plan.w_per_edge))
     if mask is not None:
         _dev(mask, torch.uint8, "mask", (e,))
+    if gate is not None:
+        _dev(gate, torch.float32, "gate", (e,))
     if out is None:
         out = torch.empty((n, plan.f_out), dtype=torch.float32, device=pos.device)
     _dev(out, torch.float32, "out", (n, plan.f_out))
     ws = _workspace(plan.workspace_size(n, e, mask is not None), pos.device, workspace)
     cella = _host_f32(cell, 9, "cell")
     args = (plan.handle, _ptr(pos), n, None if cella is None else cella.ctypes.data_as(_lib.FP),
-            _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask),
+            _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask), _ptr(gate),
             _ptr(out), _ptr(ws), ws.numel(), _stream())
     if conv_events is None:
-        check(lib.cgtp_conv_forward(*args))
+        check(lib.cgtp_conv_forward_gated(*args))
     else:
         b, t = conv_events
         check(lib.cgtp_conv_forward_timed(*args, ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(t.cuda_event)))

@@ -609,14 +609,16 @@ int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float c
 
 static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
                              const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
-                             const float* x, const float* w, const uint8_t* mask, float* out, void* workspace,
-                             size_t ws_bytes, void* stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+                             const float* x, const float* w, const uint8_t* mask, const float* gate, float* out,
+                             void* workspace, size_t ws_bytes, void* stream, hipEvent_t ev_begin,
+                             hipEvent_t ev_end) {
   int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
   if (rc != CGTP_OK) return rc;
   if (n_nodes > 0 && (!out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
   if (n_edges > 0 && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
   if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(col, 4))
     return fail(CGTP_ERR_INVALID_ARG, "x, w and out must be 16-byte aligned");
+  if (!aligned(gate, 4)) return fail(CGTP_ERR_INVALID_ARG, "gate must be 4-byte aligned");
   if (double(n_nodes) * double(P->f_in) * 4.0 >= 4294967296.0)
     return fail(CGTP_ERR_UNSUPPORTED, "x is 4 GiB or larger (32-bit byte offsets)");
   const FwdWorkspace ws = carve(*P, n_nodes, n_edges, workspace);
@@ -633,6 +635,7 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   g.col = col;
   g.shift = shift;
   g.mask = mask;
+  g.gate = gate;
   g.deg = ws.deg;
   g.act_e = ws.act_e;
   g.act_j = ws.act_j;
@@ -705,17 +708,26 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
 int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
                       const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
                       const uint8_t* mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
-  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, out, workspace,
-                           ws_bytes, stream, nullptr, nullptr);
+  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, nullptr, out,
+                           workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+int cgtp_conv_forward_gated(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
+                            const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
+                            const float* x, const float* w, const uint8_t* mask, const float* gate, float* out,
+                            void* workspace, size_t ws_bytes, void* stream) {
+  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
+                           workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
 int cgtp_conv_forward_timed(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
                             const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
-                            const float* x, const float* w, const uint8_t* mask, float* out, void* workspace,
-                            size_t ws_bytes, void* stream, void* ev_conv_begin, void* ev_conv_end) {
+                            const float* x, const float* w, const uint8_t* mask, const float* gate, float* out,
+                            void* workspace, size_t ws_bytes, void* stream, void* ev_conv_begin,
+                            void* ev_conv_end) {
   if (!ev_conv_begin || !ev_conv_end) return fail(CGTP_ERR_INVALID_ARG, "events must not be NULL");
-  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, out, workspace,
-                           ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
+  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
+                           workspace, ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
                            static_cast<hipEvent_t>(ev_conv_end));
 }
 

@@ -373,6 +373,7 @@ struct RowArgs {
   const int32_t* col;
   const int8_t* shift;
   const uint8_t* mask;
+  const float* gate;   // may be null: continuation gate per edge (0 = inactive)
   int32_t* deg;    // may be null
   int32_t* act_e;  // may be null
   int32_t* act_j;  // may be null
@@ -401,7 +402,7 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
   int cnt = 0;
   for (int b0 = rb; b0 < re; b0 += kWave) {
     const int e = b0 + lane;
-    const bool act = e < re && (!a.mask || a.mask[e] != 0);
+    const bool act = e < re && (!a.mask || a.mask[e] != 0) && (!a.gate || a.gate[e] != 0.0f);
     const unsigned long long bal = __ballot(act);
     const int slot = rb + cnt + __popcll(bal & lt_mask);
     cnt += __popcll(bal);
@@ -426,6 +427,13 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
 #pragma unroll
       for (int q = 0; q < NY; ++q) Y[q] = 0.0;
       Y[0] = 1.0;
+    }
+    // a continuation gate scales the edge's harmonics, hence its message (the product
+    // is linear in them)
+    if (a.gate) {
+      const double g = a.gate[e];
+#pragma unroll
+      for (int q = 0; q < NY; ++q) Y[q] *= g;
     }
     float* out = a.sh + (long)slot * a.sh_stride;
 #pragma unroll
@@ -556,6 +564,7 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
   a.col = p.col;
   a.shift = p.shift;
   a.mask = p.mask;
+  a.gate = p.gate;
   a.deg = p.deg;
   a.act_e = p.act_e;
   a.act_j = p.act_j;

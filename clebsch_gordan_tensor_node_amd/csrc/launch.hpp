@@ -44,6 +44,8 @@ struct RowPass {
   const int32_t* col;
   const int8_t* shift;
   const uint8_t* mask;
+  const float* gate;   // continuation gate per edge (may be null): 0 = inactive, else it
+                       // scales the stored harmonics
   int32_t* deg;
   int32_t* act_e;  // active edge ids compacted within each row (at row_ptr[i] + q)
   int32_t* act_j;  // their senders

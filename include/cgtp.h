@@ -151,16 +151,30 @@ int cgtp_conv_forward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const
                       int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
                       float* out, void* workspace, size_t ws_bytes, void* stream);
 
-/* cgtp_conv_forward, and in addition has the caller's HIP events (hipEvent_t)
- * ev_conv_begin / ev_conv_end stamped by the dispatch of the fused convolution kernel
- * itself (at the start of its first launch and the end of its last), so that the caller
- * can time that kernel apart from the prepare and harmonics passes and from launch
- * gaps.  Same kernels, same results. */
+/* The forward with BranchIP's continuation gate (BranchIP, Method: each feature is
+ * multiplied by its gate f in [0, 1] before the next tensor product, and zero-gated
+ * features are omitted — sparse evaluation).  gate: device fp32 [n_edges], 4-byte
+ * aligned, NULL = 1.  An edge is active when mask (if any) keeps it and gate[e] != 0;
+ * an active edge's message is scaled by gate[e] (the product is linear in the edge's
+ * feature), so out[i] = sum over active e of gate[e] * message_e.  w and x_j of
+ * inactive edges are never read.  Everything else as cgtp_conv_forward; the workspace
+ * size is the same. */
+int cgtp_conv_forward_gated(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
+                            const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
+                            int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
+                            const float* gate, float* out, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* cgtp_conv_forward_gated (gate may be NULL), and in addition has the caller's HIP events
+ * (hipEvent_t) ev_conv_begin / ev_conv_end stamped by the dispatch of the fused
+ * convolution kernel itself (at the start of its first launch and the end of its last),
+ * so that the caller can time that kernel apart from the prepare and harmonics passes
+ * and from launch gaps.  Same kernels, same results. */
 int cgtp_conv_forward_timed(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
                             const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
                             int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
-                            float* out, void* workspace, size_t ws_bytes, void* stream,
-                            void* ev_conv_begin, void* ev_conv_end);
+                            const float* gate, float* out, void* workspace, size_t ws_bytes,
+                            void* stream, void* ev_conv_begin, void* ev_conv_end);
 
 void cgtp_plan_destroy(cgtp_plan_t plan);
 

@@ -4,6 +4,8 @@ Bars: neighbour list and mask prepare bit-exact; edge harmonics within 2e-6 abso
 (fp64 evaluation stored as fp32); convolution relative L2 <= 1e-5 and max |diff| <= 1e-4
 over the whole output, plus bitwise run-to-run determinism.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -41,8 +43,12 @@ def _workload(name):
     rp, col, sh = O.neighbors(pos, box, wl.cutoff)
     plan = O.build_plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
     x, w, mask = WL.draw_payload(wl, rng, wl.n_atoms, plan.f_in, len(col), plan.w_per_edge)
+    _GATES[name] = WL.gate_values(wl, rng, len(col))
     _CACHE[name] = (wl, plan, pos, box, cell, rp, col, sh, x, w, mask)
     return _CACHE[name]
+
+
+_GATES = {}
 
 
 def _compare(got, ref, what):
@@ -144,10 +150,11 @@ def test_edge_sh(dev, name):
 # convolution
 # ----------------------------------------------------------------------------------
 
-def _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask, plan=None):
+def _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask, plan=None, gate=None):
     p = plan or C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
     out = C.conv_forward(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev), _t(x, dev),
-                         _t(w, dev), None if mask is None else _t(mask, dev))
+                         _t(w, dev), None if mask is None else _t(mask, dev),
+                         gate=None if gate is None else _t(gate, dev))
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -167,9 +174,11 @@ def _sub_csr(rp, rows):
     return srp, eids
 
 
-def test_conv_high_l_sampled(dev):
+@pytest.mark.parametrize("name", ["highl_768", "c4_768", "c5_768", "c6_768"])
+def test_conv_sampled_large(dev, name):
     # full-size launch on the GPU; the oracle evaluates a sample of 48 receivers
-    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("highl_768")
+    # (high L, and LunaTP Table 1 cases 4-6: 256 channels, two channel blocks at 320, L = 4)
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload(name)
     got = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask)
     rows = np.random.default_rng(0).choice(wl.n_atoms, 48, replace=False)
     srp, eids = _sub_csr(rp, rows)
@@ -180,7 +189,7 @@ def test_conv_high_l_sampled(dev):
     x_sub = np.concatenate([x[rows], x])
     rp_full = np.concatenate([srp, np.full(n, srp[-1])]).astype(np.int32)
     ref = O.conv_forward(plan, pos_sub, cell, rp_full, col_sub, sh[eids], x_sub, w[eids], None)[:len(rows)]
-    _compare(got[rows], ref, "highl_768[48 rows]")
+    _compare(got[rows], ref, f"{name}[48 rows]")
 
 
 def _small_system(n, box_len, cutoff, seed):
@@ -235,6 +244,38 @@ def test_conv_deterministic_and_nan_safe(dev):
     assert np.array_equal(a, c)
     z = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, np.zeros_like(mask))
     assert np.all(z == 0.0)
+
+
+def test_conv_gated(dev):
+    # BranchIP continuation gate on the Si system: half the edges exactly 0, the rest
+    # scale their messages; zero-gated edges are never read
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("si_gate")
+    g = _GATES["si_gate"]
+    got = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, mask, gate=g)
+    _compare(got, O.conv_forward(plan, pos, cell, rp, col, sh, x, w, mask, g), "si_gate")
+    wn = w.copy()
+    wn[g == 0] = np.nan
+    assert np.array_equal(_gpu_conv(dev, wl, pos, cell, rp, col, sh, x, wn, mask, gate=g), got)
+    # gate and mask together, on the small workload
+    wl, plan, pos, box, cell, rp, col, sh, x, w, _ = _workload("tiny")
+    rng = np.random.default_rng(11)
+    m = (rng.random(len(col)) < 0.7).astype(np.uint8)
+    g = np.where(rng.random(len(col)) < 0.3, 0.0, rng.random(len(col))).astype(np.float32)
+    got = _gpu_conv(dev, wl, pos, cell, rp, col, sh, x, w, m, gate=g)
+    _compare(got, O.conv_forward(plan, pos, cell, rp, col, sh, x, w, m, g), "tiny mask+gate")
+
+
+def test_conv_rejects_x_of_4gib(dev):
+    # the kernel addresses x with 32-bit byte offsets; the host refuses larger x before
+    # any launch (nothing is read from the undersized buffers below)
+    p = C.Plan("128x0e+64x1e+32x2e", "1x0e+1x1e+1x2e", 2, "all")
+    lib = C._lib.load()
+    buf = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    n = (1 << 32) // (4 * p.f_in) + 1
+    ptr = ctypes.c_void_p(buf.data_ptr())
+    rc = lib.cgtp_conv_forward(p.handle, ptr, n, None, ptr, ptr, None, 0, ptr, ptr, None, ptr, ptr,
+                               buf.numel() * 4, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == -3
 
 
 def test_conv_empty_graphs(dev):

@@ -25,6 +25,12 @@ Recipe (every config, seed 0, ``numpy.random.default_rng``), in draw order:
   3. x ~ N(0, 1) [N, F_in] fp32
   4. w ~ N(0, 1) [E, W] fp32
   5. mask (masked configs only): Bernoulli(0.5) per edge in CSR order, uint8.
+  6. gate (gated configs only): BranchIP continuation gate per edge in CSR order,
+     u = U[0,1), v = U[0,1) drawn as two arrays in that order, gate = 0 where u < 0.5
+     (a flat exact-zero region for half the edges) and 1 - v in (0, 1] elsewhere; fp32.
+
+LunaTP Table 1 cases 4-6 (the larger multiplicities and L = 4) are also available at the
+768-atom size as c4_768, c5_768 and c6_768.
 """
 from __future__ import annotations
 
@@ -53,6 +59,7 @@ class Workload:
     masked: bool
     seed: int = 0
     description: str = ""
+    gated: bool = False
 
 
 def _sh(lmax: int, natural: bool = True) -> str:
@@ -76,6 +83,19 @@ WORKLOADS = {
     "si_mask": Workload(
         "si_mask", 4096, 5.0, "128x0e+64x1o+32x2e+32x3o", _sh(3), 3, RULE_PARITY, "si", True,
         description="Si diamond 8x8x8 cells (4096 atoms), cutoff 5 A, Bernoulli(0.5) edge mask"),
+    "si_gate": Workload(
+        "si_gate", 4096, 5.0, "128x0e+64x1o+32x2e+32x3o", _sh(3), 3, RULE_PARITY, "si", False,
+        description="Si diamond 8x8x8 cells (4096 atoms), cutoff 5 A, continuous BranchIP gate "
+                    "(half the edges exactly 0, the rest in (0, 1])", gated=True),
+    "c4_768": Workload(
+        "c4_768", 768, 5.0, "256x0e+256x1o+256x2e+256x3o", _sh(3), 3, RULE_PARITY, "random", False,
+        description="768 random atoms, cutoff 5 A, LunaTP Table 1 case 4 irreps"),
+    "c5_768": Workload(
+        "c5_768", 768, 5.0, "320x0e+96x1o+64x2e+32x3o+32x4e", _sh(4), 4, RULE_PARITY, "random", False,
+        description="768 random atoms, cutoff 5 A, LunaTP Table 1 case 5 irreps"),
+    "c6_768": Workload(
+        "c6_768", 768, 5.0, "128x0e+128x1o+128x2e+128x3o+128x4e", _sh(4), 4, RULE_PARITY, "random", False,
+        description="768 random atoms, cutoff 5 A, LunaTP Table 1 case 6 irreps"),
 }
 
 # configuration order of the benchmark list: tiny, case-1 style, case-2 style, high-L, Si+mask
@@ -128,6 +148,15 @@ def weights(rng: np.random.Generator, n_edges: int, w_per_edge: int) -> np.ndarr
 def edge_mask(rng: np.random.Generator, n_edges: int) -> np.ndarray:
     """Draw step 5."""
     return (rng.random(n_edges) < 0.5).astype(np.uint8)
+
+
+def gate_values(wl: Workload, rng: np.random.Generator, n_edges: int):
+    """Draw step 6 (after draw_payload): the continuation gate of a gated config, else None."""
+    if not wl.gated:
+        return None
+    u = rng.random(n_edges)
+    v = rng.random(n_edges)
+    return np.where(u < 0.5, 0.0, 1.0 - v).astype(np.float32)
 
 
 def draw_payload(wl: Workload, rng: np.random.Generator, n_atoms: int, f_in: int,
