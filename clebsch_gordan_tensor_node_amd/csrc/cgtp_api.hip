@@ -676,17 +676,20 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   for (size_t li = 0; li < launches.size(); ++li) {
     const Launch& L = launches[li];
     a.n_groups = L.g1 - L.g0;
+    for (int k = 0; k < kMaxGroupsPerLaunch; ++k) a.g_start[k] = kMaxInt32;   // past the groups
     int lg_min = 6;
     for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, P->groups[k].lanes_log2);
     int per_block = 0;
     for (int k = L.g0; k < L.g1; ++k) {
       const Group& G = P->groups[k];
       a.g_start[k - L.g0] = per_block;
-      a.g_first_job[k - L.g0] = G.first_job;
-      a.g_n_jobs[k - L.g0] = G.n_jobs;
-      a.g_lanes_log2[k - L.g0] = G.lanes_log2;
-      a.g_y0[k - L.g0] = G.y0;
-      a.g_y4[k - L.g0] = G.y4;
+      GroupArgs& ga = a.grp[k - L.g0];
+      ga.start = per_block;
+      ga.first_job = G.first_job;
+      ga.n_jobs = G.n_jobs;
+      ga.lanes_log2 = G.lanes_log2;
+      ga.y0 = G.y0;
+      ga.y4 = G.y4;
       per_block += 1 << (G.lanes_log2 - lg_min);
     }
     const int64_t block = 64 >> lg_min;

@@ -45,9 +45,20 @@ struct Group {
 
 // Groups of one launch, carried in the kernel arguments.  Workgroups come in blocks of
 // 64 / 2^blk_lg_min consecutive receivers of the degree order; a block holds
-// 2^(lanes_log2 - blk_lg_min) workgroups of each group, and a workgroup finds its group
-// by an unrolled compare chain over g_start (no memory loads).
+// 2^(lanes_log2 - blk_lg_min) workgroups of each group.  A workgroup counts the groups
+// whose range starts at or before it in g_start (two wide scalar loads, no dependent
+// loads), then reads its group's record with one more.
 constexpr int kMaxGroupsPerLaunch = 32;
+
+struct alignas(32) GroupArgs {
+  int32_t start;       // first workgroup of the group inside a block
+  int32_t first_job;
+  int32_t n_jobs;
+  int32_t lanes_log2;
+  int32_t y0;
+  int32_t y4;
+  int32_t pad[2];
+};
 
 struct ConvArgs {
   const float* x;
@@ -68,11 +79,8 @@ struct ConvArgs {
   int32_t blk_wgs;            // workgroups per block of 64 / 2^blk_lg_min receivers
   int32_t blk_lg_min;         // smallest lanes_log2 of the launch's groups
   int32_t g_start[kMaxGroupsPerLaunch];       // first workgroup of each group inside a block
-  int32_t g_first_job[kMaxGroupsPerLaunch];
-  int32_t g_n_jobs[kMaxGroupsPerLaunch];
-  int32_t g_lanes_log2[kMaxGroupsPerLaunch];
-  int32_t g_y0[kMaxGroupsPerLaunch];
-  int32_t g_y4[kMaxGroupsPerLaunch];
+                                              // (INT32_MAX past the launch's groups)
+  GroupArgs grp[kMaxGroupsPerLaunch];
 };
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -216,7 +216,7 @@ constexpr int producer_depth() {
 }
 template <int K>
 constexpr int consumer_depth() {
-  return K == 4 ? 8 : 12;
+  return K == 4 ? 4 : 6;
 }
 
 __device__ __forceinline__ const float* byte_off(const float* base, uint32_t bytes) {
@@ -248,11 +248,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
   const int cap_log2 = kStageLog2 - (6 - lg);       // staged entries per receiver and window
   const int srow = (1 << cap_log2) + 1;             // stage row stride
 
-  if (tid < S) {
-    const int pos = ng * S + tid;
-    sm.slot[tid] = pos < a.n_nodes ? a.node_info[pos] : make_int4(-1, 0, 0, 0);
-  }
-  __syncthreads();
+  __syncthreads();   // the receiver records (stored by the kernel entry) are visible
   // the node order is by active degree, descending: the first receiver has the most edges
   const int qmax = __builtin_amdgcn_readfirstlane(sm.slot[0].z);
 
@@ -473,25 +469,31 @@ template <int C>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
   const int blk = int(blockIdx.x) / a.blk_wgs;
   const int wg = int(blockIdx.x) - blk * a.blk_wgs;
-  // the workgroup's group: last g with g_start[g] <= wg (unrolled, kernel-argument reads)
-  int g_base = 0, g_first = 0, g_nj = 1, lg = 0, y0 = 0, y4 = 1;
+  // the workgroup's group: the last g with g_start[g] <= wg (g_start is increasing, and
+  // INT32_MAX past the launch's groups); the sign bit of g_start - wg - 1 counts it
+  uint32_t g = 0;
 #pragma unroll
-  for (int g = 0; g < kMaxGroupsPerLaunch; ++g) {
-    if (g < a.n_groups && wg >= a.g_start[g]) {
-      g_base = a.g_start[g];
-      g_first = a.g_first_job[g];
-      g_nj = a.g_n_jobs[g];
-      lg = a.g_lanes_log2[g];
-      y0 = a.g_y0[g];
-      y4 = a.g_y4[g];
-    }
-  }
+  for (int k = 1; k < kMaxGroupsPerLaunch; ++k) g += uint32_t(a.g_start[k] - wg - 1) >> 31;
+  // read through the kernel-argument segment pointer: a dynamic index into the by-value
+  // argument would make the compiler copy the whole argument block to scratch first
+  const GroupArgs G = reinterpret_cast<const GroupArgs*>(
+      (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(ConvArgs, grp))[g];
+  const int lg = G.lanes_log2;
+  const int S = kWave >> lg;
+  const int ng = (blk << (lg - a.blk_lg_min)) + (wg - G.start);   // node group of this group
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
-  const bool has_job = wave < g_nj;
-  const Job J = a.jobs[g_first + (has_job ? wave : 0)];
+  const bool has_job = wave < G.n_jobs;
+  // the receiver records and the job descriptor are independent loads: both in flight
+  // before either is waited for
+  // (branch-free: every thread loads a valid record and stores it, the threads of one
+  // slot storing the same value, so that no divergent region separates the two loads)
+  const int tid = int(threadIdx.x);
+  const int pos = ng * S + (tid & (S - 1));
+  const int4 rec = a.node_info[min(pos, a.n_nodes - 1)];
+  const Job J = a.jobs[G.first_job + (has_job ? wave : 0)];
   __shared__ ConvSmem<C> sm;
-  const int ng = (blk << (lg - a.blk_lg_min)) + (wg - g_base);   // node group of this group
-  dispatch<C, 0, kNumVariants>(J.variant, a, J, ng, lg, y0, y4, wave, has_job, sm);
+  sm.slot[tid & (S - 1)] = pos < a.n_nodes ? rec : make_int4(-1, 0, 0, 0);
+  dispatch<C, 0, kNumVariants>(J.variant, a, J, ng, lg, G.y0, G.y4, wave, has_job, sm);
 }
 
 }  // namespace
