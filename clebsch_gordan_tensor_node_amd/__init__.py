@@ -1,4 +1,4 @@
-"""MI355X-native Clebsch-Gordan tensor-product (CGTP) convolution, forward.
+"""MI355X-native Clebsch-Gordan tensor-product (CGTP) convolution, forward (fp32; fp64 for l <= 3).
 
 Thin binding over libcgtp.so (C ABI in include/cgtp.h): argument marshalling only.
 Every step of the path (neighbour list, mask prepare, edge harmonics, the fused
@@ -42,10 +42,10 @@ class Plan:
     """A CGTP plan: irreps, paths, real-CG tables and the wave-job schedule."""
 
     def __init__(self, irreps_in: str, irreps_sh: str, l_out_max: int, path_rule="parity",
-                 host_only: bool = False):
+                 host_only: bool = False, fp64: bool = False):
         lib = load()
         h = ctypes.c_void_p()
-        flags = _lib.CGTP_PLAN_HOST_ONLY if host_only else 0
+        flags = (_lib.CGTP_PLAN_HOST_ONLY if host_only else 0) | (_lib.CGTP_PLAN_FP64 if fp64 else 0)
         check(lib.cgtp_plan_create(irreps_in.encode(), irreps_sh.encode(), int(l_out_max),
                                    _rule(path_rule), flags, ctypes.byref(h)))
         self._h = h
@@ -59,6 +59,8 @@ class Plan:
         self.sh_stride = (self.l_sh_max + 1) ** 2
         self.irreps_out = buf.value.decode()
         self.host_only = host_only
+        self.fp64 = fp64
+        self.dtype = torch.float64 if fp64 else torch.float32
 
     @property
     def handle(self):
@@ -125,6 +127,15 @@ def _host_f32(v, n, name):
     if v is None:
         return None
     a = np.ascontiguousarray(np.asarray(v.cpu() if isinstance(v, torch.Tensor) else v, dtype=np.float32).reshape(-1))
+    if a.size != n:
+        raise ValueError(f"{name} must have {n} values")
+    return a
+
+
+def _host_f64(v, n, name):
+    if v is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(v.cpu() if isinstance(v, torch.Tensor) else v, dtype=np.float64).reshape(-1))
     if a.size != n:
         raise ValueError(f"{name} must have {n} values")
     return a
@@ -203,29 +214,39 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, ou
                  conv_events=None, gate=None):
     """out[N, f_out] of the CGTP convolution (asynchronous on the current stream).
 
-    gate: optional fp32 [E] continuation gate (BranchIP): zero-gated edges are inactive,
+    gate: optional [E] continuation gate (BranchIP): zero-gated edges are inactive,
     the others' messages are scaled by the gate.
     conv_events: optional (begin, end) torch.cuda.Event pair (each recorded once before,
     so that its HIP event exists); the library records them around the fused
-    convolution kernel launches."""
+    convolution kernel launches.
+    pos, x, w, gate and out are fp32, or fp64 for a plan made with fp64=True."""
     lib = load()
-    _dev(pos, torch.float32, "pos")
+    dt = plan.dtype
+    _dev(pos, dt, "pos")
     n = pos.shape[0]
     _dev(row_ptr, torch.int32, "row_ptr", (n + 1,))
     _dev(col, torch.int32, "col")
     e = col.shape[0]
     if shift is not None:
         _dev(shift, torch.int8, "shift", (e, 3))
-    _dev(x, torch.float32, "x", (n, plan.f_in))
-    _dev(w, torch.float32, "w", (e, plan.w_per_edge))
+    _dev(x, dt, "x", (n, plan.f_in))
+    _dev(w, dt, "w", (e, plan.w_per_edge))
     if mask is not None:
         _dev(mask, torch.uint8, "mask", (e,))
     if gate is not None:
-        _dev(gate, torch.float32, "gate", (e,))
+        _dev(gate, dt, "gate", (e,))
     if out is None:
-        out = torch.empty((n, plan.f_out), dtype=torch.float32, device=pos.device)
-    _dev(out, torch.float32, "out", (n, plan.f_out))
+        out = torch.empty((n, plan.f_out), dtype=dt, device=pos.device)
+    _dev(out, dt, "out", (n, plan.f_out))
     ws = _workspace(plan.workspace_size(n, e, mask is not None), pos.device, workspace)
+    if plan.fp64:
+        cella = _host_f64(cell, 9, "cell")
+        ev = (None, None) if conv_events is None else tuple(ctypes.c_void_p(v.cuda_event) for v in conv_events)
+        check(lib.cgtp_conv_forward_f64(
+            plan.handle, _ptr(pos), n, None if cella is None else cella.ctypes.data_as(_lib.DP),
+            _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask), _ptr(gate),
+            _ptr(out), _ptr(ws), ws.numel(), _stream(), ev[0], ev[1]))
+        return out
     cella = _host_f32(cell, 9, "cell")
     args = (plan.handle, _ptr(pos), n, None if cella is None else cella.ctypes.data_as(_lib.FP),
             _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask), _ptr(gate),

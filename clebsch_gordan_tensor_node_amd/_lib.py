@@ -22,11 +22,13 @@ CGTP_ERR_CAPACITY = -4
 CGTP_PATHS_ALL = 0
 CGTP_PATHS_PARITY = 1
 CGTP_PLAN_HOST_ONLY = 1
+CGTP_PLAN_FP64 = 2
 
 EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_cg", "cgtp_plan_schedule",
     "cgtp_workspace_size", "cgtp_neighbors_workspace_size", "cgtp_neighbors_build",
-    "cgtp_conv_prepare", "cgtp_edge_sh", "cgtp_conv_forward", "cgtp_conv_forward_gated", "cgtp_conv_forward_timed", "cgtp_plan_destroy",
+    "cgtp_conv_prepare", "cgtp_edge_sh", "cgtp_conv_forward", "cgtp_conv_forward_gated", "cgtp_conv_forward_timed",
+    "cgtp_conv_forward_f64", "cgtp_plan_destroy",
     "cgtp_last_error", "cgtp_version",
 ]
 
@@ -44,6 +46,7 @@ I64 = ctypes.c_int64
 I32 = ctypes.c_int
 SZ = ctypes.c_size_t
 FP = ctypes.POINTER(ctypes.c_float)
+DP = ctypes.POINTER(ctypes.c_double)
 
 
 def load():
@@ -70,6 +73,7 @@ def load():
         "cgtp_conv_forward": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, SZ, P], I32),
         "cgtp_conv_forward_gated": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P, SZ, P], I32),
         "cgtp_conv_forward_timed": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P, SZ, P, P, P], I32),
+        "cgtp_conv_forward_f64": ([P, P, I64, DP, P, P, P, I64, P, P, P, P, P, P, SZ, P, P, P], I32),
         "cgtp_plan_destroy": ([P], None),
         "cgtp_last_error": ([], ctypes.c_char_p),
         "cgtp_version": ([], ctypes.c_char_p),

@@ -107,13 +107,15 @@ constexpr double real_cg(int l1, int l2, int l3, int m1, int m2, int m3) {
   return ((l1 + l2 + l3) % 2 == 0) ? acc.re : acc.im;
 }
 
-// Dense table for one path, fp32, index ((m1+l1)*(2l2+1) + (m2+l2))*(2l3+1) + (m3+l3).
+// Dense table for one path, fp32 and fp64, index
+// ((m1+l1)*(2l2+1) + (m2+l2))*(2l3+1) + (m3+l3).
 template <int L1, int L2, int L3>
 struct RealCG {
   static constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
   float v[N1 * N2 * N3];
+  double vd[N1 * N2 * N3];
   int nnz;
-  constexpr RealCG() : v(), nnz(0) {
+  constexpr RealCG() : v(), vd(), nnz(0) {
     for (int a = 0; a < N1; ++a)
       for (int b = 0; b < N2; ++b)
         for (int c = 0; c < N3; ++c) {
@@ -121,10 +123,19 @@ struct RealCG {
           // |values| are >= 1e-3 or exactly zero for l <= 6; snap round-off to zero
           if (x < 1e-12 && x > -1e-12) x = 0.0;
           v[(a * N2 + b) * N3 + c] = float(x);
+          vd[(a * N2 + b) * N3 + c] = x;
           nnz += (x != 0.0);
         }
   }
   constexpr float at(int a, int b, int c) const { return v[(a * N2 + b) * N3 + c]; }
+  // the coefficient in the arithmetic type of a kernel (float or double)
+  template <typename T>
+  constexpr T coef(int a, int b, int c) const {
+    if constexpr (sizeof(T) == 4)
+      return v[(a * N2 + b) * N3 + c];
+    else
+      return vd[(a * N2 + b) * N3 + c];
+  }
   // A[m1,m3] = sum_m2 C[m1,m2,m3] Y[m2] is structurally nonzero
   constexpr bool a_nonzero(int a, int c) const {
     for (int b = 0; b < N2; ++b)

@@ -142,7 +142,8 @@ struct cgtp_plan_s {
   int64_t f_in = 0, f_out = 0, w = 0;
   int l_sh_max = 0;
   int sh_stride = 1;                 // floats per SH row of cgtp_edge_sh: (l_sh_max + 1)^2
-  int sh_pad = 4;                    // floats per SH row of the forward workspace (multiple of 4)
+  int sh_pad = 4;                    // elements per SH row of the forward workspace (16-byte rows)
+  int elem = 4;                      // bytes per element of x, w, out and the workspace SH
   std::string irreps_out;
   std::vector<Job> jobs;             // ordered by group
   std::vector<Group> groups;         // by kernel class, heavy groups first
@@ -173,14 +174,15 @@ void schedule(cgtp_plan_s& P) {
   };
   std::vector<Tmp> tmp;
   std::vector<int> used(kNumVariants, 0);
-  const bool strides4 = (P.f_in % 4 == 0) && (P.f_out % 4 == 0) && (P.w % 4 == 0);
+  const int VE = 16 / P.elem;        // elements per 16-byte access
+  const bool strides4 = (P.f_in % VE == 0) && (P.f_out % VE == 0) && (P.w % VE == 0);
   int plan_lmax = 0;
   for (const PathInfo& p : P.paths) plan_lmax = std::max(plan_lmax, std::max(p.l1, std::max(p.l2, p.l3)));
   for (size_t pi = 0; pi < P.paths.size(); ++pi) {
     const PathInfo& p = P.paths[pi];
-    const bool al = strides4 && p.mul % 4 == 0 && p.in_off % 4 == 0 && p.out_off % 4 == 0 && p.w_off % 4 == 0;
-    const int K = al ? 4 : 1;
-    const int v = variant_index(p.l1, p.l2, p.l3, K);
+    const bool al = strides4 && p.mul % VE == 0 && p.in_off % VE == 0 && p.out_off % VE == 0 && p.w_off % VE == 0;
+    const int K = al ? VE : 1;
+    const int v = variant_index(p.l1, p.l2, p.l3, al ? 4 : 1);   // the vector or the scalar form
     const int cls = job_class(v, plan_lmax);
     used[v] = 1;
     std::vector<float> cg;
@@ -263,8 +265,8 @@ void schedule(cgtp_plan_s& P) {
       l2lo = std::min(l2lo, tmp[k].l2);
       l2hi = std::max(l2hi, tmp[k].l2);
     }
-    G.y0 = (l2lo * l2lo) / 4 * 4;
-    G.y4 = ((l2hi + 1) * (l2hi + 1) - G.y0 + 3) / 4;
+    G.y0 = (l2lo * l2lo) / VE * VE;
+    G.y4 = ((l2hi + 1) * (l2hi + 1) - G.y0 + VE - 1) / VE;
     // at least y4 lanes per receiver, so that the S y4 harmonic chunks of a step fit the
     // producer wave's 64 lanes (extra lanes idle)
     G.lanes_log2 = std::max(G.lanes_log2, ilog2(next_pow2(G.y4)));
@@ -287,7 +289,7 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 struct FwdWorkspace {
   int32_t *deg, *tmp_a, *tmp_b, *act_e, *act_j;
   int4* node_info;
-  float* sh;
+  void* sh;                          // [e, sh_pad] of the plan's element type
   size_t bytes;
 };
 
@@ -306,7 +308,7 @@ FwdWorkspace carve(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
   w.tmp_b = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
   w.act_e = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.act_j = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
-  w.sh = reinterpret_cast<float*>(take(size_t(e) * size_t(P.sh_pad) * 4));
+  w.sh = take(size_t(e) * size_t(P.sh_pad) * size_t(P.elem));
   w.bytes = off;
   return w;
 }
@@ -336,7 +338,8 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   *out = nullptr;
   if (path_rule != CGTP_PATHS_ALL && path_rule != CGTP_PATHS_PARITY)
     return fail(CGTP_ERR_INVALID_ARG, "unknown path rule %d", path_rule);
-  if (flags & ~unsigned(CGTP_PLAN_HOST_ONLY)) return fail(CGTP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  if (flags & ~unsigned(CGTP_PLAN_HOST_ONLY | CGTP_PLAN_FP64))
+    return fail(CGTP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   if (l_out_max < 0) return fail(CGTP_ERR_INVALID_ARG, "l_out_max < 0");
   auto P = new cgtp_plan_s();
   std::string err;
@@ -413,7 +416,16 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   P->l_sh_max = 0;
   for (const Irrep& r : P->sh) P->l_sh_max = std::max(P->l_sh_max, r.l);
   P->sh_stride = (P->l_sh_max + 1) * (P->l_sh_max + 1);
-  P->sh_pad = (P->sh_stride + 3) / 4 * 4;
+  P->elem = (flags & CGTP_PLAN_FP64) ? 8 : 4;
+  P->sh_pad = (P->sh_stride + 16 / P->elem - 1) / (16 / P->elem) * (16 / P->elem);
+  if (P->elem == 8) {
+    int lmax = 0;
+    for (const PathInfo& p : P->paths) lmax = std::max(lmax, std::max(p.l1, std::max(p.l2, p.l3)));
+    if (lmax > 3) {
+      delete P;
+      return fail(CGTP_ERR_UNSUPPORTED, "fp64 plans support l <= 3 (this plan reaches l = %d)", lmax);
+    }
+  }
   P->irreps_out = format_irreps(P->out);
   schedule(*P);
 
@@ -584,10 +596,15 @@ int cgtp_conv_prepare(cgtp_plan_t P, const int32_t* row_ptr, const uint8_t* mask
   return ok();
 }
 
-static void fill_cell(RowPass& g, const float* cell) {
+}  // extern "C"
+
+template <typename T>
+static void fill_cell(RowPass& g, const T* cell) {
   g.has_cell = cell != nullptr;
   for (int k = 0; k < 9; ++k) g.cell[k] = cell ? double(cell[k]) : 0.0;
 }
+
+extern "C" {
 
 int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
                  const int32_t* col, const int8_t* shift, int64_t n_edges, float* sh, void* stream) {
@@ -607,19 +624,26 @@ int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float c
   return ok();
 }
 
-static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
+}  // extern "C"
+
+// The forward in element type T (float, or double for plans made with CGTP_PLAN_FP64).
+template <typename T>
+static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const T cell[9],
                              const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
-                             const float* x, const float* w, const uint8_t* mask, const float* gate, float* out,
+                             const T* x, const T* w, const uint8_t* mask, const T* gate, T* out,
                              void* workspace, size_t ws_bytes, void* stream, hipEvent_t ev_begin,
                              hipEvent_t ev_end) {
   int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
   if (rc != CGTP_OK) return rc;
+  if (P->elem != int(sizeof(T)))
+    return fail(CGTP_ERR_INVALID_ARG, "the plan's precision (%s) does not match this entry point (%s)",
+                P->elem == 8 ? "fp64" : "fp32", sizeof(T) == 8 ? "fp64" : "fp32");
   if (n_nodes > 0 && (!out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
   if (n_edges > 0 && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(pos, 4) || !aligned(col, 4))
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16) || !aligned(pos, sizeof(T)) || !aligned(col, 4))
     return fail(CGTP_ERR_INVALID_ARG, "x, w and out must be 16-byte aligned");
-  if (!aligned(gate, 4)) return fail(CGTP_ERR_INVALID_ARG, "gate must be 4-byte aligned");
-  if (double(n_nodes) * double(P->f_in) * 4.0 >= 4294967296.0)
+  if (!aligned(gate, sizeof(T))) return fail(CGTP_ERR_INVALID_ARG, "gate must be aligned to its element size");
+  if (double(n_nodes) * double(P->f_in) * double(sizeof(T)) >= 4294967296.0)
     return fail(CGTP_ERR_UNSUPPORTED, "x is 4 GiB or larger (32-bit byte offsets)");
   const FwdWorkspace ws = carve(*P, n_nodes, n_edges, workspace);
   if (!workspace || ws_bytes < ws.bytes)
@@ -630,16 +654,22 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
 
   // 1. per row: active degree and the harmonics of its active edges (CSR order)
   RowPass g{};
-  g.pos = pos;
+  if constexpr (sizeof(T) == 8) {
+    g.pos64 = pos;
+    g.gate64 = gate;
+    g.sh64 = static_cast<double*>(ws.sh);
+  } else {
+    g.pos = pos;
+    g.gate = gate;
+    g.sh = static_cast<float*>(ws.sh);
+  }
   g.row_ptr = row_ptr;
   g.col = col;
   g.shift = shift;
   g.mask = mask;
-  g.gate = gate;
   g.deg = ws.deg;
   g.act_e = ws.act_e;
   g.act_j = ws.act_j;
-  g.sh = ws.sh;
   g.sh_stride = P->sh_pad;
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
@@ -649,10 +679,10 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   CGTP_HIP(launch_degree_order(ws.deg, int(n_nodes), row_ptr, ws.node_info, s));
   // 3. the fused convolution: per kernel class, launches of up to kMaxGroupsPerLaunch
   //    job groups whose workgroup ranges travel in the kernel arguments
-  ConvArgs a{};
+  ConvArgsT<T> a{};
   a.x = x;
   a.w = w;
-  a.sh = ws.sh;
+  a.sh = static_cast<const T*>(ws.sh);
   a.node_info = ws.node_info;
   a.act_e = ws.act_e;
   a.act_j = ws.act_j;
@@ -708,10 +738,12 @@ static int conv_forward_impl(cgtp_plan_t P, const float* pos, int64_t n_nodes, c
   return ok();
 }
 
+extern "C" {
+
 int cgtp_conv_forward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
                       const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
                       const uint8_t* mask, float* out, void* workspace, size_t ws_bytes, void* stream) {
-  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, nullptr, out,
+  return conv_forward_impl<float>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, nullptr, out,
                            workspace, ws_bytes, stream, nullptr, nullptr);
 }
 
@@ -719,8 +751,18 @@ int cgtp_conv_forward_gated(cgtp_plan_t P, const float* pos, int64_t n_nodes, co
                             const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
                             const float* x, const float* w, const uint8_t* mask, const float* gate, float* out,
                             void* workspace, size_t ws_bytes, void* stream) {
-  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
+  return conv_forward_impl<float>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
                            workspace, ws_bytes, stream, nullptr, nullptr);
+}
+
+int cgtp_conv_forward_f64(cgtp_plan_t P, const double* pos, int64_t n_nodes, const double cell[9],
+                          const int32_t* row_ptr, const int32_t* col, const int8_t* shift, int64_t n_edges,
+                          const double* x, const double* w, const uint8_t* mask, const double* gate, double* out,
+                          void* workspace, size_t ws_bytes, void* stream, void* ev_conv_begin,
+                          void* ev_conv_end) {
+  return conv_forward_impl<double>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out, workspace,
+                           ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
+                           static_cast<hipEvent_t>(ev_conv_end));
 }
 
 int cgtp_conv_forward_timed(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
@@ -729,7 +771,7 @@ int cgtp_conv_forward_timed(cgtp_plan_t P, const float* pos, int64_t n_nodes, co
                             void* workspace, size_t ws_bytes, void* stream, void* ev_conv_begin,
                             void* ev_conv_end) {
   if (!ev_conv_begin || !ev_conv_end) return fail(CGTP_ERR_INVALID_ARG, "events must not be NULL");
-  return conv_forward_impl(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
+  return conv_forward_impl<float>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out,
                            workspace, ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
                            static_cast<hipEvent_t>(ev_conv_end));
 }

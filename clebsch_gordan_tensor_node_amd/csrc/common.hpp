@@ -60,20 +60,21 @@ struct alignas(32) GroupArgs {
   int32_t pad[2];
 };
 
-struct ConvArgs {
-  const float* x;
-  const float* w;
-  const float* sh;            // harmonics of active edges, compacted within each row
+template <typename T>
+struct ConvArgsT {
+  const T* x;
+  const T* w;
+  const T* sh;                // harmonics of active edges, compacted within each row
   const int4* node_info;      // per order position: {node, row_ptr[node], active degree, 0}
   const int32_t* act_e;       // active edge ids, compacted within each row (at row_ptr[i] + q)
   const int32_t* act_j;       // their senders
-  float* out;
+  T* out;
   const Job* jobs;            // the plan's job table
   int32_t n_nodes;
   int32_t f_in;
   int32_t f_out;
   int32_t w_stride;
-  int32_t sh_stride;          // floats per SH row (a multiple of 4)
+  int32_t sh_stride;          // elements per SH row (a multiple of 16 / sizeof(T))
   int32_t n_groups;           // groups of this launch (<= kMaxGroupsPerLaunch)
   int32_t total_wgs;          // workgroups of this launch (whole blocks)
   int32_t blk_wgs;            // workgroups per block of 64 / 2^blk_lg_min receivers
@@ -82,6 +83,9 @@ struct ConvArgs {
                                               // (INT32_MAX past the launch's groups)
   GroupArgs grp[kMaxGroupsPerLaunch];
 };
+using ConvArgs = ConvArgsT<float>;
+// the kernel classes (l <= 3) that are also built in fp64
+constexpr int kNumClassesF64 = 2;
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

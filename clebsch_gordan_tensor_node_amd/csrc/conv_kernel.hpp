@@ -29,7 +29,9 @@
 // The uvu coupling is not a dense contraction, so no MFMA is used.
 //
 // This header is compiled once per kernel class (kernels_conv.hip with
-// CGTP_CONV_CLASS = 0 .. kNumClasses-1); each build instantiates one conv_kernel.
+// CGTP_CONV_CLASS = 0 .. kNumClasses-1); each build instantiates the class's conv_kernel
+// for fp32 and, for the classes with l <= 3, for fp64 (T = double: the same design with
+// 16-byte chunks of two elements).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -61,68 +63,78 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int L1, int L2, int L3>
 inline constexpr RealCG<L1, L2, L3> kCG{};
 
+// Elements of T in one 16-byte vector access (4 floats, 2 doubles).  A job's K is either
+// that (16-byte aligned data) or 1.
+template <typename T>
+inline constexpr int kVec = int(16 / sizeof(T));
+
+template <typename T>
+__device__ __forceinline__ T fma_t(T a, T b, T c) {
+  if constexpr (sizeof(T) == 4)
+    return __builtin_fmaf(a, b, c);
+  else
+    return __builtin_fma(a, b, c);
+}
+
 // A[M1, M3] = sum_m2 C[M1, m2, M3] Y[m2], structural zeros skipped.
-template <int L1, int L2, int L3, int M1, int M3>
-__device__ __forceinline__ float a_entry(const float* Y) {
-  float s = 0.0f;
+template <typename T, int L1, int L2, int L3, int M1, int M3>
+__device__ __forceinline__ T a_entry(const T* Y) {
+  T s = T(0);
   bool first = true;
   static_for<0, 2 * L2 + 1>([&](auto M2) {
-    constexpr float c = kCG<L1, L2, L3>.at(M1, decltype(M2)::value, M3);
-    if constexpr (c != 0.0f) {
+    constexpr T c = kCG<L1, L2, L3>.template coef<T>(M1, decltype(M2)::value, M3);
+    if constexpr (c != T(0)) {
       if (first) {
         s = c * Y[decltype(M2)::value];
         first = false;
       } else {
-        s = __builtin_fmaf(c, Y[decltype(M2)::value], s);
+        s = fma_t(c, Y[decltype(M2)::value], s);
       }
     }
   });
   return s;
 }
 
-template <int K>
-__device__ __forceinline__ void load_k(const float* __restrict__ p, float* v) {
-  if constexpr (K == 4) {
-    const float4 q = *reinterpret_cast<const float4*>(p);
-    v[0] = q.x;
-    v[1] = q.y;
-    v[2] = q.z;
-    v[3] = q.w;
+template <typename T>
+using vec16_t = T __attribute__((ext_vector_type(kVec<T>)));
+
+template <typename T, int K>
+__device__ __forceinline__ void load_k(const T* __restrict__ p, T* v) {
+  if constexpr (K == kVec<T>) {
+    const vec16_t<T> q = *reinterpret_cast<const vec16_t<T>*>(p);
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = q[k];
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = p[k];
   }
 }
 
-// K floats read once (the weights): a non-temporal load, so that the stream does not
+// K elements read once (the weights): a non-temporal load, so that the stream does not
 // evict the x rows and harmonics that the producer gathers again and again from L2
-template <int K>
-__device__ __forceinline__ void load_k_stream(const float* __restrict__ p, float* v) {
-  if constexpr (K == 4) {
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4 q = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
-    v[0] = q[0];
-    v[1] = q[1];
-    v[2] = q[2];
-    v[3] = q[3];
+template <typename T, int K>
+__device__ __forceinline__ void load_k_stream(const T* __restrict__ p, T* v) {
+  if constexpr (K == kVec<T>) {
+    const vec16_t<T> q = __builtin_nontemporal_load(reinterpret_cast<const vec16_t<T>*>(p));
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = q[k];
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = __builtin_nontemporal_load(p + k);
   }
 }
 
-// n contiguous floats, n a multiple of 4 when K == 4 (16-byte aligned source)
-template <int K, int N>
-__device__ __forceinline__ void load_run(const float* __restrict__ p, float* v) {
-  if constexpr (K == 4) {
-    static_assert(N % 4 == 0, "vector run");
+// N contiguous elements, in 16-byte vectors when K is the vector width (16-byte aligned
+// source, N a multiple of K)
+template <typename T, int K, int N>
+__device__ __forceinline__ void load_run(const T* __restrict__ p, T* v) {
+  if constexpr (K == kVec<T>) {
+    static_assert(N % K == 0, "vector run");
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      const float4 t = reinterpret_cast<const float4*>(p)[q];
-      v[4 * q + 0] = t.x;
-      v[4 * q + 1] = t.y;
-      v[4 * q + 2] = t.z;
-      v[4 * q + 3] = t.w;
+    for (int q = 0; q < N / K; ++q) {
+      const vec16_t<T> t = reinterpret_cast<const vec16_t<T>*>(p)[q];
+#pragma unroll
+      for (int k = 0; k < K; ++k) v[K * q + k] = t[k];
     }
   } else {
 #pragma unroll
@@ -130,18 +142,16 @@ __device__ __forceinline__ void load_run(const float* __restrict__ p, float* v) 
   }
 }
 
-template <int K, int N>
-__device__ __forceinline__ void store_run(float* __restrict__ p, const float* v) {
-  if constexpr (K == 4) {
-    static_assert(N % 4 == 0, "vector run");
+template <typename T, int K, int N>
+__device__ __forceinline__ void store_run(T* __restrict__ p, const T* v) {
+  if constexpr (K == kVec<T>) {
+    static_assert(N % K == 0, "vector run");
 #pragma unroll
-    for (int q = 0; q < N / 4; ++q) {
-      float4 t;
-      t.x = v[4 * q + 0];
-      t.y = v[4 * q + 1];
-      t.z = v[4 * q + 2];
-      t.w = v[4 * q + 3];
-      reinterpret_cast<float4*>(p)[q] = t;
+    for (int q = 0; q < N / K; ++q) {
+      vec16_t<T> t;
+#pragma unroll
+      for (int k = 0; k < K; ++k) t[k] = v[K * q + k];
+      reinterpret_cast<vec16_t<T>*>(p)[q] = t;
     }
   } else {
 #pragma unroll
@@ -150,8 +160,8 @@ __device__ __forceinline__ void store_run(float* __restrict__ p, const float* v)
 }
 
 // acc[k, m3] += w[k] sum_m1 A[m1, m3] x[k, m1] with A = C . Y (one edge, K channels)
-template <int L1, int L2, int L3, int K>
-__device__ __forceinline__ void accumulate_edge(float* acc, float* xv, const float* wv, const float* Y) {
+template <typename T, int L1, int L2, int L3, int K>
+__device__ __forceinline__ void accumulate_edge(T* acc, T* xv, const T* wv, const T* Y) {
   constexpr int N1 = 2 * L1 + 1, N3 = 2 * L3 + 1;
   if constexpr (N1 <= N3) {
     // scale the input side (2l1+1 products per channel), accumulate A x directly
@@ -162,9 +172,9 @@ __device__ __forceinline__ void accumulate_edge(float* acc, float* xv, const flo
       static_for<0, N1>([&](auto M1c) {
         constexpr int M1 = decltype(M1c)::value;
         if constexpr (kCG<L1, L2, L3>.a_nonzero(M1, M3)) {
-          const float A = a_entry<L1, L2, L3, M1, M3>(Y);
+          const T A = a_entry<T, L1, L2, L3, M1, M3>(Y);
 #pragma unroll
-          for (int k = 0; k < K; ++k) acc[k * N3 + M3] = __builtin_fmaf(A, xv[k * N1 + M1], acc[k * N3 + M3]);
+          for (int k = 0; k < K; ++k) acc[k * N3 + M3] = fma_t(A, xv[k * N1 + M1], acc[k * N3 + M3]);
         }
       });
     });
@@ -172,32 +182,32 @@ __device__ __forceinline__ void accumulate_edge(float* acc, float* xv, const flo
     // form sum_m1 A x per output component, then scale by w (2l3+1 per channel)
     static_for<0, N3>([&](auto M3c) {
       constexpr int M3 = decltype(M3c)::value;
-      float tk[K];
+      T tk[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) tk[k] = 0.0f;
+      for (int k = 0; k < K; ++k) tk[k] = T(0);
       static_for<0, N1>([&](auto M1c) {
         constexpr int M1 = decltype(M1c)::value;
         if constexpr (kCG<L1, L2, L3>.a_nonzero(M1, M3)) {
-          const float A = a_entry<L1, L2, L3, M1, M3>(Y);
+          const T A = a_entry<T, L1, L2, L3, M1, M3>(Y);
 #pragma unroll
-          for (int k = 0; k < K; ++k) tk[k] = __builtin_fmaf(A, xv[k * N1 + M1], tk[k]);
+          for (int k = 0; k < K; ++k) tk[k] = fma_t(A, xv[k * N1 + M1], tk[k]);
         }
       });
 #pragma unroll
-      for (int k = 0; k < K; ++k) acc[k * N3 + M3] = __builtin_fmaf(wv[k], tk[k], acc[k * N3 + M3]);
+      for (int k = 0; k < K; ++k) acc[k * N3 + M3] = fma_t(wv[k], tk[k], acc[k * N3 + M3]);
     });
   }
 }
 
 // LDS of one workgroup of class C (sized by the class's largest l1).  Per step the
 // producer wave stores N1 x chunks and one harmonic chunk per lane; chunk c of a step
-// sits at c * (chunk floats), so the stage is receiver-major.  Chunks past the step's
+// sits at c * (chunk elements), so the stage is receiver-major.  Chunks past the step's
 // data land in the padding.
-template <int C>
+template <int C, typename T>
 struct ConvSmem {
   static constexpr int kN1 = 2 * class_max_l1(C) + 1;
-  float x[2][kWave * kN1 * 4];      // x_j segments of one step (double-buffered)
-  float y[2][kWave * 4];            // harmonics of one step (double-buffered)
+  T x[2][kWave * kN1 * kVec<T>];    // x_j segments of one step (double-buffered)
+  T y[2][kWave * kVec<T>];          // harmonics of one step (double-buffered)
   // staged offsets, receiver r's window at r (cap + 1): the odd row stride puts the
   // receivers of one read on different LDS banks
   uint32_t sx[(1 << kStageLog2) + kWave];   // j f_in (x element offset of the sender's row)
@@ -206,41 +216,45 @@ struct ConvSmem {
   int4 slot[kWave];                 // receiver records {node or -1, row start, active degree, 0}
 };
 
-// Pipeline depths (edge steps whose loads are in flight while one step is used).  The
-// producer's loads (x_j rows, harmonics) mostly hit the L2 cache and need few steps;
-// the consumers' weight loads come from HBM once and get a deep ring of K floats a slot.
-template <int N1, int K>
+// Pipeline depths (edge steps whose loads are in flight while one step is used), sized
+// by the 32-bit registers a step holds.  The producer's loads (x_j rows, harmonics)
+// mostly hit the L2 cache and need few steps; the consumers' weight loads come from HBM
+// once and get a ring of K elements a slot.
+template <typename T, int N1, int K>
 constexpr int producer_depth() {
-  constexpr int d = 72 / (N1 * K + 4);
+  constexpr int d = 72 / ((N1 * K + kVec<T>) * int(sizeof(T) / 4));
   return d < 2 ? 2 : (d > 4 ? 4 : d);
 }
-template <int K>
+template <typename T, int K>
 constexpr int consumer_depth() {
-  return K == 4 ? 4 : 6;
+  return K == kVec<T> ? 4 : 6;
 }
 
-__device__ __forceinline__ const float* byte_off(const float* base, uint32_t bytes) {
-  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + bytes);
+template <typename T>
+__device__ __forceinline__ const T* byte_off(const T* base, uint32_t bytes) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + bytes);
 }
 
 // One wave of a workgroup.  Waves 0 .. kConvJobs-1 are consumers, one job each (or idle
 // when the group has fewer jobs); wave kConvJobs is the producer.  Consumer lane layout:
 // lane = (receiver slot ns, channel lane t) with T = 2^lg channel lanes and S = 64 / T
 // receivers (node positions ng S .. ng S + S - 1).  Stage layout per step: receiver r's
-// x_j segment (n_ch N1 floats) at r n_ch N1, cut into chunks of K floats, chunk c loaded
-// by producer lane c mod 64; receiver r's harmonics Y[y0 .. y0 + 4 y4) at r 4 y4 (the
-// schedule keeps S y4 <= 64: one 16-byte chunk per producer lane).
+// x_j segment (n_ch N1 elements) at r n_ch N1, cut into chunks of K elements, chunk c
+// loaded by producer lane c mod 64; receiver r's harmonics Y[y0 .. y0 + V y4) at r V y4,
+// V = kVec<T> (the schedule keeps S y4 <= 64: one 16-byte chunk per producer lane).
 //
 // Steps past a receiver's last active edge repeat that edge (its offsets are staged
 // again) with the weight replaced by zero, so every load is of real, finite data; a
 // receiver without active edges stores zeros.  Every load of a pipeline step is issued
 // unconditionally: a skipped load would make the wave's in-order memory counter
 // ambiguous and force full waits.
-template <int C, int L1, int L2, int L3, int K>
-__device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng, int lg, int y0, int y4, int wave,
-                                        bool has_job, ConvSmem<C>& sm) {
+template <int C, typename T, int L1, int L2, int L3, int K>
+__device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int ng, int lg, int y0, int y4,
+                                        int wave, bool has_job, ConvSmem<C, T>& sm) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  static_assert(N1 <= ConvSmem<C>::kN1, "x stage too small for this variant");
+  constexpr int V = kVec<T>;
+  constexpr uint32_t B = sizeof(T);
+  static_assert(N1 <= ConvSmem<C, T>::kN1, "x stage too small for this variant");
   const int tid = int(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int S = kWave >> lg;
@@ -279,7 +293,7 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
 
   if (wave == kConvJobs) {
     // ---------------- producer: x_j segments and harmonics of every step ----------------
-    constexpr int D = producer_depth<N1, K>();
+    constexpr int D = producer_depth<T, N1, K>();
     const int cps = n_ch * N1 / K;                  // x chunks per receiver
     uint32_t x_off[N1];
     int x_sl[N1];
@@ -295,16 +309,16 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
       }
     }
     int y_sl = 0;
-    const float* ybase = a.sh + y0;
+    const T* ybase = a.sh + y0;
     if (lane < S * y4) {
       const int r = lane / y4;
       const int4 si = sm.slot[r];
       y_sl = r * srow;
-      ybase = a.sh + (long)(si.z > 0 ? si.y : 0) * a.sh_stride + y0 + 4 * (lane - r * y4);
+      ybase = a.sh + (long)(si.z > 0 ? si.y : 0) * a.sh_stride + y0 + V * (lane - r * y4);
     }
     struct PSlot {
-      float x[N1 * K];
-      float y[4];
+      T x[N1 * K];
+      T y[V];
     };
     struct PIdx {
       uint32_t x[N1];
@@ -318,26 +332,22 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
       auto fetch = [&](int k, PIdx& ix) {
         const int kk = min(k, steps - 1);
 #pragma unroll
-        for (int i = 0; i < N1; ++i) ix.x[i] = (sm.sx[x_sl[i] + kk] + x_off[i]) * 4u;
-        ix.y = sm.sy[y_sl + kk] * 4u;
+        for (int i = 0; i < N1; ++i) ix.x[i] = (sm.sx[x_sl[i] + kk] + x_off[i]) * B;
+        ix.y = sm.sy[y_sl + kk] * B;
       };
       auto issue = [&](const PIdx& ix, PSlot& b) {
 #pragma unroll
-        for (int i = 0; i < N1; ++i) load_k<K>(byte_off(a.x, ix.x[i]), b.x + i * K);
-        const float4 v = *reinterpret_cast<const float4*>(byte_off(ybase, ix.y));
-        b.y[0] = v.x;
-        b.y[1] = v.y;
-        b.y[2] = v.z;
-        b.y[3] = v.w;
+        for (int i = 0; i < N1; ++i) load_k<T, K>(byte_off(a.x, ix.x[i]), b.x + i * K);
+        load_k<T, V>(byte_off(ybase, ix.y), b.y);
         // keep the steps' loads in program order: the memory counter is in order, and a
         // step's loads scheduled after a later step's would make that step wait for both
         __builtin_amdgcn_sched_barrier(0);
       };
       auto publish = [&](int k, PSlot& b) {
-        float* xs = sm.x[k & 1];
+        T* xs = sm.x[k & 1];
 #pragma unroll
-        for (int i = 0; i < N1; ++i) store_run<K, K>(xs + (lane + kWave * i) * K, b.x + i * K);
-        store_run<4, 4>(sm.y[k & 1] + lane * 4, b.y);
+        for (int i = 0; i < N1; ++i) store_run<T, K, K>(xs + (lane + kWave * i) * K, b.x + i * K);
+        store_run<T, V, V>(sm.y[k & 1] + lane * V, b.y);
         __syncthreads();
       };
       // every step issues its loads unconditionally (past the window's end they repeat
@@ -376,32 +386,32 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
   }
 
   // ---------------- consumer: this job's weights and accumulation ----------------
-  constexpr int D = consumer_depth<K>();
+  constexpr int D = consumer_depth<T, K>();
   const int t = lane & ((1 << lg) - 1);
   const int ns = lane >> lg;
   const int ch0 = t * K;
   const int4 my = sm.slot[ns];
   const int w_n = ch0 < n_ch ? my.z : 0;
   const int w_sl = ns * srow;
-  const float* __restrict__ wbase =
+  const T* __restrict__ wbase =
       a.w + (long)(my.z > 0 ? my.y : 0) * a.w_stride + J.w_off + (ch0 < n_ch ? ch0 : 0);
   const int x_rd = (ns * n_ch + ch0) * N1;          // this lane's operands in the x stage
-  const int y_rd = ns * 4 * y4 + J.sh_off - y0;     // ... and its Y_l2 in the harmonic stage
+  const int y_rd = ns * V * y4 + J.sh_off - y0;     // ... and its Y_l2 in the harmonic stage
 
-  float acc[K * N3];
+  T acc[K * N3];
 #pragma unroll
-  for (int q = 0; q < K * N3; ++q) acc[q] = 0.0f;
-  float ring[D][K];
+  for (int q = 0; q < K * N3; ++q) acc[q] = T(0);
+  T ring[D][K];
   for (int qw = 0; qw < qmax; qw += (1 << cap_log2)) {
     const int steps = min(1 << cap_log2, qmax - qw);
     stage(qw, steps);
     __syncthreads();
-    auto fetch = [&](int k) { return sm.sw[w_sl + min(k, steps - 1)] * 4u; };
-    auto issue = [&](uint32_t ow, float* b) {
-      load_k_stream<K>(byte_off(wbase, ow), b);
+    auto fetch = [&](int k) { return sm.sw[w_sl + min(k, steps - 1)] * B; };
+    auto issue = [&](uint32_t ow, T* b) {
+      load_k_stream<T, K>(byte_off(wbase, ow), b);
       __builtin_amdgcn_sched_barrier(0);   // loads stay in step order (see the producer)
     };
-    auto use = [&](int k, float* b) {
+    auto use = [&](int k, T* b) {
       __syncthreads();   // the producer has published step k
       // the weights are first touched here, after the barrier: without this the
       // scheduler hoists the selects of all unrolled steps above the loop's barriers and
@@ -409,16 +419,16 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
 #pragma unroll
       for (int m = 0; m < K; ++m) asm volatile("" : "+v"(b[m]));
       const bool live = qw + k < w_n;
-      float wv[K];
+      T wv[K];
 #pragma unroll
-      for (int m = 0; m < K; ++m) wv[m] = live ? b[m] : 0.0f;
-      float xv[K * N1];
-      load_run<K, K * N1>(sm.x[k & 1] + x_rd, xv);
-      float Y[N2];
-      const float* ys = sm.y[k & 1] + y_rd;
+      for (int m = 0; m < K; ++m) wv[m] = live ? b[m] : T(0);
+      T xv[K * N1];
+      load_run<T, K, K * N1>(sm.x[k & 1] + x_rd, xv);
+      T Y[N2];
+      const T* ys = sm.y[k & 1] + y_rd;
 #pragma unroll
       for (int m = 0; m < N2; ++m) Y[m] = ys[m];
-      accumulate_edge<L1, L2, L3, K>(acc, xv, wv, Y);
+      accumulate_edge<T, L1, L2, L3, K>(acc, xv, wv, Y);
     };
     // as in the producer: loads unconditional, only the use skipped past the end
     static_for<0, D - 1>([&](auto P) {
@@ -439,34 +449,35 @@ __device__ __forceinline__ void run_job(const ConvArgs& a, const Job& J, int ng,
   if (ch0 < n_ch && my.x >= 0) {
     if (my.z == 0) {
 #pragma unroll
-      for (int q = 0; q < K * N3; ++q) acc[q] = 0.0f;
+      for (int q = 0; q < K * N3; ++q) acc[q] = T(0);
     }
-    store_run<K, K * N3>(a.out + (long)my.x * a.f_out + J.out_off + ch0 * N3, acc);
+    store_run<T, K, K * N3>(a.out + (long)my.x * a.f_out + J.out_off + ch0 * N3, acc);
   }
 }
 
-template <int C, int LO, int HI>
-__device__ __forceinline__ void dispatch(int v, const ConvArgs& a, const Job& J, int ng, int lg, int y0, int y4,
-                                         int wave, bool has_job, ConvSmem<C>& sm) {
+template <int C, typename T, int LO, int HI>
+__device__ __forceinline__ void dispatch(int v, const ConvArgsT<T>& a, const Job& J, int ng, int lg, int y0, int y4,
+                                         int wave, bool has_job, ConvSmem<C, T>& sm) {
   if constexpr (HI - LO == 1) {
     if constexpr (class_contains(C, LO)) {
       constexpr VariantDesc d = variant_desc(LO);
-      run_job<C, d.l1, d.l2, d.l3, d.k>(a, J, ng, lg, y0, y4, wave, has_job, sm);
+      constexpr int K = d.k == 1 ? 1 : kVec<T>;   // the vector form moves 16 bytes per lane
+      run_job<C, T, d.l1, d.l2, d.l3, K>(a, J, ng, lg, y0, y4, wave, has_job, sm);
     }
   } else {
     constexpr int MID = (LO + HI) / 2;
     if (v < MID)
-      dispatch<C, LO, MID>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
+      dispatch<C, T, LO, MID>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
     else
-      dispatch<C, MID, HI>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
+      dispatch<C, T, MID, HI>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
   }
 }
 
 // One workgroup per (group, node group): the producer wave and one consumer wave per job
 // (consumer waves past the group's job count only keep the barrier count).  The producer
 // runs the first job's code path, which fixes l1, K and the channel block it gathers.
-template <int C>
-__global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
+template <int C, typename T>
+__global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgsT<T> a) {
   const int blk = int(blockIdx.x) / a.blk_wgs;
   const int wg = int(blockIdx.x) - blk * a.blk_wgs;
   // the workgroup's group: the last g with g_start[g] <= wg (g_start is increasing, and
@@ -477,7 +488,7 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
   // read through the kernel-argument segment pointer: a dynamic index into the by-value
   // argument would make the compiler copy the whole argument block to scratch first
   const GroupArgs G = reinterpret_cast<const GroupArgs*>(
-      (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(ConvArgs, grp))[g];
+      (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(ConvArgsT<T>, grp))[g];
   const int lg = G.lanes_log2;
   const int S = kWave >> lg;
   const int ng = (blk << (lg - a.blk_lg_min)) + (wg - G.start);   // node group of this group
@@ -491,22 +502,22 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgs a) {
   const int pos = ng * S + (tid & (S - 1));
   const int4 rec = a.node_info[min(pos, a.n_nodes - 1)];
   const Job J = a.jobs[G.first_job + (has_job ? wave : 0)];
-  __shared__ ConvSmem<C> sm;
+  __shared__ ConvSmem<C, T> sm;
   sm.slot[tid & (S - 1)] = pos < a.n_nodes ? rec : make_int4(-1, 0, 0, 0);
-  dispatch<C, 0, kNumVariants>(J.variant, a, J, ng, lg, G.y0, G.y4, wave, has_job, sm);
+  dispatch<C, T, 0, kNumVariants>(J.variant, a, J, ng, lg, G.y0, G.y4, wave, has_job, sm);
 }
 
 }  // namespace
 
-template <int C>
-hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+template <int C, typename T>
+hipError_t launch_conv_class(const ConvArgsT<T>& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   if (args.total_wgs <= 0) return hipSuccess;
   const int blocks = args.total_wgs;
   if (ev_start || ev_stop) {
     // the events are stamped by the dispatch itself: kernel time without launch gaps
-    hipExtLaunchKernelGGL(conv_kernel<C>, dim3(blocks), dim3(kConvThreads), 0, s, ev_start, ev_stop, 0, args);
+    hipExtLaunchKernelGGL(conv_kernel<C, T>, dim3(blocks), dim3(kConvThreads), 0, s, ev_start, ev_stop, 0, args);
   } else {
-    conv_kernel<C><<<blocks, kConvThreads, 0, s>>>(args);
+    conv_kernel<C, T><<<blocks, kConvThreads, 0, s>>>(args);
   }
   return hipGetLastError();
 }

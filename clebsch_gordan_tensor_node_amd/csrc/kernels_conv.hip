@@ -7,6 +7,10 @@
 #endif
 
 namespace cgtp {
-template hipError_t launch_conv_class<CGTP_CONV_CLASS>(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start,
-                                                       hipEvent_t ev_stop);
+template hipError_t launch_conv_class<CGTP_CONV_CLASS, float>(const ConvArgsT<float>& args, hipStream_t s,
+                                                              hipEvent_t ev_start, hipEvent_t ev_stop);
+#if CGTP_CONV_CLASS < 2
+template hipError_t launch_conv_class<CGTP_CONV_CLASS, double>(const ConvArgsT<double>& args, hipStream_t s,
+                                                               hipEvent_t ev_start, hipEvent_t ev_stop);
+#endif
 }  // namespace cgtp

@@ -367,17 +367,19 @@ __global__ void __launch_bounds__(kScanThreads) degree_order_kernel(const int32_
 // harmonics in fp64, stored fp32.
 // ---------------------------------------------------------------------------------
 
+// P: element type of the positions, the gate and the stored harmonics (float or double)
+template <typename P>
 struct RowArgs {
-  const float* pos;
+  const P* pos;
   const int32_t* row_ptr;
   const int32_t* col;
   const int8_t* shift;
   const uint8_t* mask;
-  const float* gate;   // may be null: continuation gate per edge (0 = inactive)
+  const P* gate;   // may be null: continuation gate per edge (0 = inactive)
   int32_t* deg;    // may be null
   int32_t* act_e;  // may be null
   int32_t* act_j;  // may be null
-  float* sh;       // may be null
+  P* sh;           // may be null
   int n_nodes;
   int has_cell;
   int sh_stride;
@@ -389,8 +391,8 @@ constexpr int kRowThreads = 256;
 // Row i's active edges are written compacted within the row's own CSR segment: the
 // q-th active edge of row i goes to slot row_ptr[i] + q (q from a ballot prefix).  With
 // no mask the slot is the edge itself.
-template <int L>
-__global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
+template <int L, typename P>
+__global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs<P> a) {
   const int row = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kRowThreads / kWave) + int(threadIdx.x) / kWave);
   if (row >= a.n_nodes) return;
   const int lane = lane_id();
@@ -402,7 +404,7 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
   int cnt = 0;
   for (int b0 = rb; b0 < re; b0 += kWave) {
     const int e = b0 + lane;
-    const bool act = e < re && (!a.mask || a.mask[e] != 0) && (!a.gate || a.gate[e] != 0.0f);
+    const bool act = e < re && (!a.mask || a.mask[e] != 0) && (!a.gate || a.gate[e] != P(0));
     const unsigned long long bal = __ballot(act);
     const int slot = rb + cnt + __popcll(bal & lt_mask);
     cnt += __popcll(bal);
@@ -435,10 +437,10 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs a) {
 #pragma unroll
       for (int q = 0; q < NY; ++q) Y[q] *= g;
     }
-    float* out = a.sh + (long)slot * a.sh_stride;
+    P* out = a.sh + (long)slot * a.sh_stride;
 #pragma unroll
-    for (int q = 0; q < NY; ++q) out[q] = float(Y[q]);
-    for (int q = NY; q < a.sh_stride; ++q) out[q] = 0.0f;
+    for (int q = 0; q < NY; ++q) out[q] = P(Y[q]);
+    for (int q = NY; q < a.sh_stride; ++q) out[q] = P(0);
   }
   if (a.deg && lane == 0) a.deg[row] = cnt;
 }
@@ -553,35 +555,55 @@ hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrW
   return hipGetLastError();
 }
 
-hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
-  if (p.n_nodes == 0) return hipSuccess;
-  if (!p.row_ptr) return hipErrorInvalidValue;
-  if ((p.sh || p.act_j) && p.n_edges > 0 && !p.col) return hipErrorInvalidValue;
-  if (p.sh && p.n_edges > 0 && !p.pos) return hipErrorInvalidValue;
-  RowArgs a{};
-  a.pos = p.pos;
+template <typename P>
+static RowArgs<P> row_args(const RowPass& p, const P* pos, const P* gate, P* sh, int l_sh_max) {
+  RowArgs<P> a{};
+  a.pos = pos;
   a.row_ptr = p.row_ptr;
   a.col = p.col;
   a.shift = p.shift;
   a.mask = p.mask;
-  a.gate = p.gate;
+  a.gate = gate;
   a.deg = p.deg;
   a.act_e = p.act_e;
   a.act_j = p.act_j;
-  a.sh = p.sh;
+  a.sh = sh;
   a.n_nodes = p.n_nodes;
   a.has_cell = p.has_cell;
   a.sh_stride = p.sh_stride > 0 ? p.sh_stride : (l_sh_max + 1) * (l_sh_max + 1);
   for (int k = 0; k < 9; ++k) a.cell[k] = p.cell[k];
+  return a;
+}
+
+hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
+  if (p.n_nodes == 0) return hipSuccess;
+  if (!p.row_ptr) return hipErrorInvalidValue;
+  const bool f64 = p.pos64 || p.gate64 || p.sh64;
+  if (f64 && (p.pos || p.gate || p.sh)) return hipErrorInvalidValue;   // one element type per pass
+  const bool has_sh = p.sh || p.sh64;
+  if ((has_sh || p.act_j) && p.n_edges > 0 && !p.col) return hipErrorInvalidValue;
+  if (has_sh && p.n_edges > 0 && !(p.pos || p.pos64)) return hipErrorInvalidValue;
   const int nb = ceil_div(p.n_nodes, kRowThreads / kWave);
+  if (f64) {
+    const RowArgs<double> a = row_args<double>(p, p.pos64, p.gate64, p.sh64, l_sh_max);
+    switch (l_sh_max) {
+      case 0: edge_rows_kernel<0, double><<<nb, kRowThreads, 0, s>>>(a); break;
+      case 1: edge_rows_kernel<1, double><<<nb, kRowThreads, 0, s>>>(a); break;
+      case 2: edge_rows_kernel<2, double><<<nb, kRowThreads, 0, s>>>(a); break;
+      case 3: edge_rows_kernel<3, double><<<nb, kRowThreads, 0, s>>>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const RowArgs<float> a = row_args<float>(p, p.pos, p.gate, p.sh, l_sh_max);
   switch (l_sh_max) {
-    case 0: edge_rows_kernel<0><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 1: edge_rows_kernel<1><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 2: edge_rows_kernel<2><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 3: edge_rows_kernel<3><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 4: edge_rows_kernel<4><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 5: edge_rows_kernel<5><<<nb, kRowThreads, 0, s>>>(a); break;
-    case 6: edge_rows_kernel<6><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 0: edge_rows_kernel<0, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 1: edge_rows_kernel<1, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 2: edge_rows_kernel<2, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 3: edge_rows_kernel<3, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 4: edge_rows_kernel<4, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 5: edge_rows_kernel<5, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    case 6: edge_rows_kernel<6, float><<<nb, kRowThreads, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -607,20 +629,29 @@ hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int
   return hipGetLastError();
 }
 
-hipError_t launch_conv(const ConvArgs& args, int cls, hipStream_t s, hipEvent_t b, hipEvent_t e) {
+hipError_t launch_conv(const ConvArgsT<float>& args, int cls, hipStream_t s, hipEvent_t b, hipEvent_t e) {
   switch (cls) {
-    case 0: return launch_conv_class<0>(args, s, b, e);
-    case 1: return launch_conv_class<1>(args, s, b, e);
-    case 2: return launch_conv_class<2>(args, s, b, e);
-    case 3: return launch_conv_class<3>(args, s, b, e);
-    case 4: return launch_conv_class<4>(args, s, b, e);
-    case 5: return launch_conv_class<5>(args, s, b, e);
-    case 6: return launch_conv_class<6>(args, s, b, e);
-    case 7: return launch_conv_class<7>(args, s, b, e);
-    case 8: return launch_conv_class<8>(args, s, b, e);
+    case 0: return launch_conv_class<0, float>(args, s, b, e);
+    case 1: return launch_conv_class<1, float>(args, s, b, e);
+    case 2: return launch_conv_class<2, float>(args, s, b, e);
+    case 3: return launch_conv_class<3, float>(args, s, b, e);
+    case 4: return launch_conv_class<4, float>(args, s, b, e);
+    case 5: return launch_conv_class<5, float>(args, s, b, e);
+    case 6: return launch_conv_class<6, float>(args, s, b, e);
+    case 7: return launch_conv_class<7, float>(args, s, b, e);
+    case 8: return launch_conv_class<8, float>(args, s, b, e);
     default: return hipErrorInvalidValue;
   }
 }
+
+hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hipEvent_t b, hipEvent_t e) {
+  switch (cls) {
+    case 0: return launch_conv_class<0, double>(args, s, b, e);
+    case 1: return launch_conv_class<1, double>(args, s, b, e);
+    default: return hipErrorInvalidValue;
+  }
+}
+static_assert(kNumClassesF64 == 2, "launch_conv covers every fp64 kernel class");
 
 static_assert(kNumClasses == 9, "launch_conv covers every kernel class");
 

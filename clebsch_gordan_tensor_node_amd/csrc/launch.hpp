@@ -37,7 +37,9 @@ hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrW
 
 // Per-row pass: active-edge count per row and, compacted within each row's CSR segment,
 // the active edge ids, senders and harmonics (sh [n_edges, (l_sh_max+1)^2]).  Every
-// output may be null.  Without a mask the slots are the edges themselves.
+// output may be null.  Without a mask the slots are the edges themselves.  The fp64
+// fields (pos64, gate64, sh64; l_sh_max <= 3) replace pos, gate and sh for an fp64
+// forward; one pass uses one element type.
 struct RowPass {
   const float* pos;
   const int32_t* row_ptr;
@@ -50,6 +52,9 @@ struct RowPass {
   int32_t* act_e;  // active edge ids compacted within each row (at row_ptr[i] + q)
   int32_t* act_j;  // their senders
   float* sh;       // their harmonics, same slots
+  const double* pos64;
+  const double* gate64;
+  double* sh64;
   int sh_stride;   // floats per SH row (0: (l_sh_max + 1)^2); entries past (l_sh_max + 1)^2 are zeroed
   int n_nodes;
   int n_edges;
@@ -73,11 +78,13 @@ hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int
                           int n_edges, int32_t* act_eid, hipStream_t s);
 
 // The fused conv kernel of one variant class over `args.total_wgs` workgroups (one per
-// job group and node group; one explicit instantiation per class, each in its own
-// translation unit).
+// job group and node group; one explicit instantiation per class and element type,
+// each class in its own translation unit; fp64 for the classes below kNumClassesF64).
 // ev_start / ev_stop (may be null): HIP events stamped at this launch's start / end.
-template <int C>
-hipError_t launch_conv_class(const ConvArgs& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_conv(const ConvArgs& args, int cls, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+template <int C, typename T>
+hipError_t launch_conv_class(const ConvArgsT<T>& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_conv(const ConvArgsT<float>& args, int cls, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hipEvent_t ev_start,
+                       hipEvent_t ev_stop);
 
 }  // namespace cgtp

@@ -1,6 +1,6 @@
 /*
  * cgtp.h -- C ABI of libcgtp.so: the Clebsch-Gordan tensor-product (CGTP)
- * convolution, forward, for AMD Instinct MI355X (gfx950).
+ * convolution, forward (fp32, and fp64 for l <= 3), for AMD Instinct MI355X (gfx950).
  *
  * What is computed (the pages print no formula; this is the textbook definition that
  * LunaTP's abstract says its kernels preserve):
@@ -72,9 +72,14 @@ enum {
 
 enum { CGTP_PATHS_ALL = 0, CGTP_PATHS_PARITY = 1 };
 
-/* Plan flag: build host tables only (no device upload).  Such a plan answers the
- * query calls but cgtp_conv_* return CGTP_ERR_INVALID_ARG with it. */
-enum { CGTP_PLAN_HOST_ONLY = 1u };
+/* Plan flags.  CGTP_PLAN_HOST_ONLY: build host tables only (no device upload); such a
+ * plan answers the query calls but cgtp_conv_* return CGTP_ERR_INVALID_ARG with it.
+ * CGTP_PLAN_FP64: the plan's forward runs in fp64 (LunaTP reports its kernels in
+ * double precision: Figure 8, Table 11); it is used with cgtp_conv_forward_f64 only,
+ * supports l <= 3 (else CGTP_ERR_UNSUPPORTED), and its workspace holds fp64
+ * harmonics.  The fp32 forward entry points return CGTP_ERR_INVALID_ARG with an fp64
+ * plan and cgtp_conv_forward_f64 with an fp32 plan. */
+enum { CGTP_PLAN_HOST_ONLY = 1u, CGTP_PLAN_FP64 = 2u };
 
 /* Parse irreps, enumerate paths, build the real-CG tables and the wave-job schedule,
  * and (unless CGTP_PLAN_HOST_ONLY) upload the job table to the current device.
@@ -175,6 +180,20 @@ int cgtp_conv_forward_timed(cgtp_plan_t plan, const float* pos, int64_t n_nodes,
                             int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
                             const float* gate, float* out, void* workspace, size_t ws_bytes,
                             void* stream, void* ev_conv_begin, void* ev_conv_end);
+
+/* The forward in double precision, for plans created with CGTP_PLAN_FP64 (LunaTP,
+ * Figure 8 and Table 11: the kernels are measured in fp64).  Same definition,
+ * semantics and integer arguments as cgtp_conv_forward_gated; pos [n_nodes, 3], cell
+ * (host, may be NULL), x, w, gate (may be NULL) and out are fp64, x, w and out 16-byte
+ * aligned, pos and gate 8-byte aligned; x must be smaller than 4 GiB.  Geometry,
+ * harmonics, coefficients and accumulation are fp64.  ev_conv_begin / ev_conv_end
+ * (hipEvent_t, may be NULL) are stamped as in cgtp_conv_forward_timed.  The workspace
+ * size is cgtp_workspace_size of the same plan. */
+int cgtp_conv_forward_f64(cgtp_plan_t plan, const double* pos, int64_t n_nodes, const double cell[9],
+                          const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
+                          int64_t n_edges, const double* x, const double* w, const uint8_t* mask,
+                          const double* gate, double* out, void* workspace, size_t ws_bytes,
+                          void* stream, void* ev_conv_begin, void* ev_conv_end);
 
 void cgtp_plan_destroy(cgtp_plan_t plan);
 

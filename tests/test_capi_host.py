@@ -19,7 +19,7 @@ C = pytest.importorskip("clebsch_gordan_tensor_node_amd")
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "cgtp.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(cgtp_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(cgtp_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -103,3 +103,33 @@ def test_workspace_size_monotone():
     assert lib.cgtp_neighbors_workspace_size(100, box.ctypes.data_as(C._lib.FP), 3.0, ctypes.byref(sz)) == 0
     assert sz.value > 0
     assert lib.cgtp_neighbors_workspace_size(100, box.ctypes.data_as(C._lib.FP), -1.0, ctypes.byref(sz)) == -1
+
+
+@pytest.mark.parametrize("name", ["tiny", "c1_768", "c2_768", "si_mask"])
+def test_fp64_plan_host(name):
+    # an fp64 plan has the fp32 plan's layout; only its schedule (16-byte chunks of two
+    # elements) and its workspace (fp64 harmonics) differ
+    wl = WL.WORKLOADS[name]
+    p32 = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule, host_only=True)
+    p64 = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule, host_only=True, fp64=True)
+    assert (p64.f_in, p64.f_out, p64.w_per_edge, p64.n_paths) == (p32.f_in, p32.f_out, p32.w_per_edge, p32.n_paths)
+    assert np.array_equal(p64.paths(), p32.paths())
+    nj, nv = p64.schedule()
+    assert nj >= p64.n_paths and nv >= 1
+    assert p64.workspace_size(768, 20000) > p32.workspace_size(768, 20000)
+
+
+def test_fp64_plan_limits():
+    with pytest.raises(C.CgtpError) as e:        # fp64 kernels are built for l <= 3
+        C.Plan("8x0e+8x4e", "1x0e+1x1o", 4, "all", host_only=True, fp64=True)
+    assert e.value.code == -3
+    with pytest.raises(C.CgtpError) as e:
+        C.Plan("8x1o", "1x0e+1x4e", 3, "all", host_only=True, fp64=True)
+    assert e.value.code == -3
+    lib = C._lib.load()
+    h = ctypes.c_void_p()
+    assert lib.cgtp_plan_create(b"8x0e", b"1x0e", 0, 0, 4, ctypes.byref(h)) == -1   # unknown flag
+    p = C.Plan("8x0e+8x3o", "1x0e+1x3o", 3, "all", host_only=True, fp64=True)
+    rc = lib.cgtp_conv_forward_f64(p.handle, None, 0, None, None, None, None, 0, None, None, None, None,
+                                   None, None, 0, None, None, None)
+    assert rc == -1 and b"HOST_ONLY" in lib.cgtp_last_error()
