@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the CGTP convolution forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1_768]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1_768] [--dtype f32|f64]
 
 One step = one pass of the hot path over resident inputs: mask prepare (active CSR and
 degree order), per-edge compaction and harmonics, and the fused convolution kernel(s).
@@ -43,10 +43,11 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, dtype: str = "f32"):
     """HBM bytes per conv launch from the committed counter summary, if it was taken on
     the current kernel sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"conv_kernel_{workload}_pmc.txt")
+    tag = workload if dtype == "f32" else f"{workload}_{dtype}"
+    path = os.path.join(ROOT, "profiles", f"conv_kernel_{tag}_pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -94,6 +95,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c1_768")
+    ap.add_argument("--dtype", choices=["f32", "f64"], default="f32",
+                    help="arithmetic type of the forward (f64: plans with l <= 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-warm-cache", action="store_true",
@@ -143,9 +146,16 @@ def main(argv=None) -> int:
         t_nbr.append(time.perf_counter() - t0)
     n, e = wl.n_atoms, int(col.shape[0])
 
-    plan = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    f64 = a.dtype == "f64"
+    elem = 8 if f64 else 4
+    plan = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule, fp64=f64)
     x, w, mask = WL.draw_payload(wl, rng, n, plan.f_in, e, plan.w_per_edge)
     gate = WL.gate_values(wl, rng, e)
+    if f64:   # the same draws, exact in fp64
+        x, w = x.astype(np.float64), w.astype(np.float64)
+        gate = None if gate is None else gate.astype(np.float64)
+        pos_d = pos_d.double()
+        cell = None if cell is None else np.asarray(cell, dtype=np.float64)
     active = np.ones(e, dtype=bool)
     if mask is not None:
         active &= mask != 0
@@ -159,7 +169,7 @@ def main(argv=None) -> int:
     k = min(64, max(3, math.ceil(ROTATE_BYTES / max(w_bytes, 1))))
     w0 = torch.from_numpy(w).to(dev)
     wbufs = [w0] + [w0.clone() for _ in range(k - 1)]
-    outs = [torch.empty((n, plan.f_out), dtype=torch.float32, device=dev) for _ in range(k)]
+    outs = [torch.empty((n, plan.f_out), dtype=plan.dtype, device=dev) for _ in range(k)]
     ws = torch.empty(plan.workspace_size(n, e, mask is not None), dtype=torch.uint8, device=dev)
 
     def step(s, evs=None):
@@ -205,16 +215,16 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         ms_warm = t_beg.elapsed_time(t_end) / K
 
-    # algorithmic bytes of the hot path, each moved once: the weights of the active edges
-    # (4 W per active edge), the edge list (4 col + 3 shift, + 1 mask byte when masked,
-    # + 4 gate bytes when gated, per edge), the row pointers (4 (N + 1)), 12 bytes of
-    # positions per node, and the node features in and the outputs out (4 F_in and
-    # 4 F_out per node)
-    conv_bytes = (4 * plan.w_per_edge * e_act
-                  + e * (4 + 3 + (1 if mask is not None else 0) + (4 if gate is not None else 0))
-                  + 4 * (n + 1) + 12 * n + 4 * plan.f_in * n + 4 * plan.f_out * n)
+    # algorithmic bytes of the hot path, each moved once (b = 4 bytes per element in
+    # fp32, 8 in fp64): the weights of the active edges (b W per active edge), the edge
+    # list (4 col + 3 shift, + 1 mask byte when masked, + b gate bytes when gated, per
+    # edge), the row pointers (4 (N + 1)), 3 b bytes of positions per node, and the node
+    # features in and the outputs out (b F_in and b F_out per node)
+    conv_bytes = (elem * plan.w_per_edge * e_act
+                  + e * (4 + 3 + (1 if mask is not None else 0) + (elem if gate is not None else 0))
+                  + 4 * (n + 1) + 3 * elem * n + elem * plan.f_in * n + elem * plan.f_out * n)
     achieved = conv_bytes / (conv_ms * 1e-3) / 1e9
-    traffic = read_traffic(wl.name)
+    traffic = read_traffic(wl.name, a.dtype)
 
     out = {
         "metric": METRIC,
@@ -227,7 +237,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": a.dtype,
         "data": "synthetic",
         "config": {"workload": wl.name, "n_atoms": n, "n_edges": e, "n_active_edges": e_act,
                    "cutoff": wl.cutoff, "irreps_in": wl.irreps_in, "irreps_sh": wl.irreps_sh,
