@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the Clebsch-Gordan tensor-product (CGTP) convolution, forward.
+"""fp64 CPU oracle of the Clebsch-Gordan tensor-product (CGTP) convolution, forward and
+gradients.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``; never by the product package, and it imports
@@ -506,6 +507,106 @@ def conv_forward_loops(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=No
 
 
 # --------------------------------------------------------------------------------------
+# Gradients of the convolution (the backward pass; LunaTP Abstract: its kernels cover the
+# derivatives that forces need).  The forward is trilinear in (x_j, w_e, Y(r_e)), so the
+# gradients of a scalar L with dL/d out = grad_out are its adjoints, written out:
+#   dL/dw[e, c_p(u)]       = g_e sum_{m1,m2,m3} C_p[m1,m2,m3] x[j,u,m1] Y[m2] gout[i,c_p(u),m3]
+#   dL/dx[j, u, m1]       += g_e w[e,c_p(u)] sum_{m2,m3} C_p[m1,m2,m3] Y[m2] gout[i,c_p(u),m3]
+#   dL/dY_{l2}[e, m2]     += g_e w[e,c_p(u)] sum_{m1,m3} C_p[m1,m2,m3] x[j,u,m1] gout[i,c_p(u),m3]
+#   dL/dr_e                = sum_{l2,m2} dL/dY[e, m2] dY_{l2,m2}/dr (r_e)
+#   dL/dpos[j] += dL/dr_e,  dL/dpos[i] -= dL/dr_e          (r_e = pos[j] - pos[i] + ...)
+# with g_e the continuation gate (1 without one); inactive edges have zero gradients and
+# contribute nothing.  The gate, mask, cell and shifts are constants.
+# --------------------------------------------------------------------------------------
+
+def real_sh_grad(l: int, vec: np.ndarray) -> np.ndarray:
+    """dY_l(vec/|vec|)/d vec for vec of shape [..., 3]; returns [..., 2l+1, 3] fp64.
+
+    Spherical coordinates of real_sh: Y = N P(cos theta) T(m phi) with T = cos or sin, so
+    grad Y = (e_theta dY/dtheta + e_phi (1/sin theta) dY/dphi) / |vec|, with
+    dP_l^m(cos theta)/dtheta = (l cos theta P_l^m - (l+m) P_{l-1}^m) / sin theta (the
+    standard recurrence (x^2 - 1) dP_l^m/dx = l x P_l^m - (l+m) P_{l-1}^m, any fixed
+    phase convention) and e_theta = (cos t cos p, cos t sin p, -sin t),
+    e_phi = (-sin p, cos p, 0).  Undefined on the z axis (sin theta = 0) and at the
+    origin: those raise.  l = 0 has zero gradient."""
+    v = np.asarray(vec, dtype=np.float64)
+    shp = v.shape[:-1]
+    v = v.reshape(-1, 3)
+    out = np.zeros((v.shape[0], 2 * l + 1, 3))
+    if l == 0 or v.shape[0] == 0:
+        return out.reshape(*shp, 2 * l + 1, 3)
+    r = np.sqrt((v * v).sum(axis=1))
+    rho = np.sqrt(v[:, 0] ** 2 + v[:, 1] ** 2)
+    if np.any(r == 0.0) or np.any(rho <= 1e-12 * r):
+        raise ValueError("real_sh_grad: a vector is zero or on the z axis")
+    ct, st = v[:, 2] / r, rho / r
+    phi = np.arctan2(v[:, 1], v[:, 0])
+    cp, sp = np.cos(phi), np.sin(phi)
+    e_t = np.stack([ct * cp, ct * sp, -st], axis=1)
+    e_p = np.stack([-sp, cp, np.zeros_like(sp)], axis=1)
+    for m in range(0, l + 1):
+        pl = (-1) ** m * scipy.special.lpmv(m, l, ct)
+        plm1 = (-1) ** m * scipy.special.lpmv(m, l - 1, ct) if m <= l - 1 else np.zeros_like(ct)
+        dpl = (l * ct * pl - (l + m) * plm1) / st            # d P_l^m(cos theta) / d theta
+        if m == 0:
+            nrm = math.sqrt(2 * l + 1)
+            out[:, l, :] = (nrm * dpl)[:, None] * e_t
+        else:
+            nrm = math.sqrt(2.0) * math.sqrt((2 * l + 1) * math.factorial(l - m) / math.factorial(l + m))
+            cm, sm = np.cos(m * phi), np.sin(m * phi)
+            # + m: N P cos(m phi);  - m: N P sin(m phi)
+            out[:, l + m, :] = (nrm * dpl * cm)[:, None] * e_t + (nrm * pl * (-m * sm) / st)[:, None] * e_p
+            out[:, l - m, :] = (nrm * dpl * sm)[:, None] * e_t + (nrm * pl * (m * cm) / st)[:, None] * e_p
+    out /= r[:, None, None]
+    return out.reshape(*shp, 2 * l + 1, 3)
+
+
+def conv_backward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, grad_out, mask=None, gate=None):
+    """Gradients (grad_x [N, F_in], grad_w [E, W], grad_pos [N, 3]) of a scalar L whose
+    gradient with respect to conv_forward's output is grad_out [N, F_out]; fp64.
+    Inactive edges get grad_w rows of exactly 0 and their w and x_j are never read."""
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    n = row_ptr.shape[0] - 1
+    e_all = len(col)
+    xf = np.asarray(x, dtype=np.float64)
+    wf = np.asarray(w, dtype=np.float64)
+    gf = np.asarray(grad_out, dtype=np.float64)
+    grad_x = np.zeros((n, plan.f_in))
+    grad_w = np.zeros((e_all, plan.w_per_edge))
+    grad_pos = np.zeros((n, 3))
+    _, act_eid, _ = prepare(row_ptr, _active_mask(mask, gate, e_all))
+    ids = act_eid.astype(np.int64)
+    if ids.size == 0:
+        return grad_x, grad_w, grad_pos
+    recv = np.repeat(np.arange(n), np.diff(row_ptr))
+    i = recv[ids]
+    j = np.asarray(col, dtype=np.int64)[ids]
+    r = edge_vectors(pos, cell, row_ptr, col, shift, ids)
+    g = np.ones(ids.size) if gate is None else np.asarray(gate, dtype=np.float64)[ids]
+    Y = {l: real_sh(l, r) for _, l, _ in plan.irreps_sh}
+    gY = {l: np.zeros((ids.size, 2 * l + 1)) for _, l, _ in plan.irreps_sh}
+    for p in plan.paths:
+        n1, n3 = 2 * p.l1 + 1, 2 * p.l3 + 1
+        C = real_cg(p.l1, p.l2, p.l3)
+        xj = xf[j, p.in_off:p.in_off + p.mul * n1].reshape(-1, p.mul, n1)
+        gi = gf[i, p.out_off:p.out_off + p.mul * n3].reshape(-1, p.mul, n3)
+        wv = wf[ids, p.w_off:p.w_off + p.mul]
+        A = np.einsum("abc,eb->eac", C, Y[p.l2])                       # [E_act, n1, n3]
+        t = np.matmul(xj, A)                                            # [E_act, mul, n3]
+        grad_w[ids, p.w_off:p.w_off + p.mul] += g[:, None] * (t * gi).sum(axis=2)
+        gx = np.einsum("eac,euc->eua", A, gi) * (g[:, None] * wv)[:, :, None]
+        np.add.at(grad_x[:, p.in_off:p.in_off + p.mul * n1], j, gx.reshape(ids.size, -1))
+        gY[p.l2] += np.einsum("abc,eua,euc,eu->eb", C, xj, gi, g[:, None] * wv)
+    grad_r = np.zeros((ids.size, 3))
+    for _, l, _ in plan.irreps_sh:
+        if l > 0:
+            grad_r += np.einsum("eb,ebk->ek", gY[l], real_sh_grad(l, r))
+    np.add.at(grad_pos, j, grad_r)
+    np.add.at(grad_pos, i, -grad_r)
+    return grad_x, grad_w, grad_pos
+
+
+# --------------------------------------------------------------------------------------
 # Cost model of the plain formulation, for reporting only.
 # --------------------------------------------------------------------------------------
 
@@ -517,5 +618,5 @@ __all__ = [
     "PATHS_ALL", "PATHS_PARITY", "parse_irreps", "format_irreps", "Path", "Plan",
     "build_plan", "cg_complex", "u_matrix", "real_cg", "real_cg_residual", "real_sh",
     "wigner_d_real", "random_rotation", "neighbors", "prepare", "edge_vectors",
-    "edge_sh", "conv_forward", "conv_forward_loops", "cg_nnz",
+    "edge_sh", "conv_forward", "conv_forward_loops", "real_sh_grad", "conv_backward", "cg_nnz",
 ]
