@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import CGTP_PATHS_ALL, CGTP_PATHS_PARITY, CgtpError, check, load
 
-__all__ = ["Plan", "neighbors_build", "conv_prepare", "edge_sh", "conv_forward", "CgtpError",
+__all__ = ["Plan", "neighbors_build", "conv_prepare", "edge_sh", "conv_forward", "conv_backward", "CgtpError",
            "CGTP_PATHS_ALL", "CGTP_PATHS_PARITY", "library_path", "version"]
 
 
@@ -89,6 +89,11 @@ class Plan:
         b = ctypes.c_size_t()
         check(load().cgtp_workspace_size(self.handle, int(n_nodes), int(n_edges), int(bool(has_mask)),
                                          ctypes.byref(b)))
+        return b.value
+
+    def backward_workspace_size(self, n_nodes: int, n_edges: int) -> int:
+        b = ctypes.c_size_t()
+        check(load().cgtp_backward_workspace_size(self.handle, int(n_nodes), int(n_edges), ctypes.byref(b)))
         return b.value
 
     def close(self):
@@ -257,3 +262,35 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, ou
         b, t = conv_events
         check(lib.cgtp_conv_forward_timed(*args, ctypes.c_void_p(b.cuda_event), ctypes.c_void_p(t.cuda_event)))
     return out
+
+
+def conv_backward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, grad_out, mask=None, gate=None,
+                  need=("x", "w", "pos"), workspace=None):
+    """Gradients of a scalar L with dL/d out = grad_out [N, f_out] (fp32, l <= 3 plans):
+    returns (grad_x [N, f_in], grad_w [E, W], grad_pos [N, 3]); an entry not in `need`
+    is None.  Asynchronous on the current stream."""
+    lib = load()
+    _dev(pos, torch.float32, "pos")
+    n = pos.shape[0]
+    _dev(row_ptr, torch.int32, "row_ptr", (n + 1,))
+    _dev(col, torch.int32, "col")
+    e = col.shape[0]
+    if shift is not None:
+        _dev(shift, torch.int8, "shift", (e, 3))
+    _dev(x, torch.float32, "x", (n, plan.f_in))
+    _dev(w, torch.float32, "w", (e, plan.w_per_edge))
+    _dev(grad_out, torch.float32, "grad_out", (n, plan.f_out))
+    if mask is not None:
+        _dev(mask, torch.uint8, "mask", (e,))
+    if gate is not None:
+        _dev(gate, torch.float32, "gate", (e,))
+    dev = pos.device
+    gx = torch.empty((n, plan.f_in), dtype=torch.float32, device=dev) if "x" in need else None
+    gw = torch.empty((e, plan.w_per_edge), dtype=torch.float32, device=dev) if "w" in need else None
+    gp = torch.empty((n, 3), dtype=torch.float32, device=dev) if "pos" in need else None
+    ws = _workspace(plan.backward_workspace_size(n, e), dev, workspace)
+    cella = _host_f32(cell, 9, "cell")
+    check(lib.cgtp_conv_backward(plan.handle, _ptr(pos), n, None if cella is None else cella.ctypes.data_as(_lib.FP),
+                                 _ptr(row_ptr), _ptr(col), _ptr(shift), e, _ptr(x), _ptr(w), _ptr(mask), _ptr(gate),
+                                 _ptr(grad_out), _ptr(gx), _ptr(gw), _ptr(gp), _ptr(ws), ws.numel(), _stream()))
+    return gx, gw, gp

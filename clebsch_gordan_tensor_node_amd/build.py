@@ -40,7 +40,8 @@ def _hipcc() -> str:
 
 
 def _units():
-    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o")]
+    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o"),
+             ("kernels_bwd.hip", [], "kernels_bwd.o")]
     for c in range(N_CONV_CLASSES):
         units.append(("kernels_conv.hip", [f"-DCGTP_CONV_CLASS={c}"], f"kernels_conv_c{c}.o"))
     return units

@@ -151,8 +151,16 @@ struct cgtp_plan_s {
   int n_variants = 0;
   bool host_only = true;
   int device = -1;
-  void* d_tables = nullptr;          // device copy of the job table
+  void* d_tables = nullptr;          // device copy of the job, path and irrep tables
   Job* d_jobs = nullptr;
+  // backward tables: one record per path, and the paths of each input irrep as
+  // [start (n_in + 1) | paths (n_paths) | l (n_in) | mul (n_in) | offset (n_in)]
+  std::vector<PathDev> pdev;
+  std::vector<int32_t> irrep_tab;
+  int gy_stride = 0;                 // sum over paths of 2 l2 + 1
+  int lmax = 0;                      // largest l of the plan
+  PathDev* d_paths = nullptr;
+  int32_t* d_irrep = nullptr;
 };
 
 namespace {
@@ -428,6 +436,48 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   }
   P->irreps_out = format_irreps(P->out);
   schedule(*P);
+  // backward tables
+  P->gy_stride = 0;
+  P->lmax = 0;
+  for (const PathInfo& p : P->paths) {
+    PathDev d{};
+    d.variant = variant_index(p.l1, p.l2, p.l3, 1);
+    d.l1 = p.l1;
+    d.l2 = p.l2;
+    d.l3 = p.l3;
+    d.mul = p.mul;
+    d.in_off = p.in_off;
+    d.out_off = p.out_off;
+    d.w_off = p.w_off;
+    d.sh_off = p.l2 * p.l2;
+    d.gy_off = P->gy_stride;
+    d.i_in = p.i_in;
+    P->gy_stride += 2 * p.l2 + 1;
+    P->lmax = std::max(P->lmax, std::max(p.l1, std::max(p.l2, p.l3)));
+    P->pdev.push_back(d);
+  }
+  {
+    const int ni = int(P->in.size());
+    std::vector<int32_t> start(ni + 1, 0), list;
+    for (int a = 0; a < ni; ++a) {
+      for (size_t q = 0; q < P->paths.size(); ++q)
+        if (P->paths[q].i_in == a) list.push_back(int32_t(q));
+      start[a + 1] = int32_t(list.size());
+    }
+    P->irrep_tab = start;
+    P->irrep_tab.insert(P->irrep_tab.end(), list.begin(), list.end());
+    int64_t off_in = 0;
+    std::vector<int32_t> ls, ms, os;
+    for (const Irrep& r : P->in) {
+      ls.push_back(r.l);
+      ms.push_back(r.mul);
+      os.push_back(int32_t(off_in));
+      off_in += int64_t(r.mul) * (2 * r.l + 1);
+    }
+    P->irrep_tab.insert(P->irrep_tab.end(), ls.begin(), ls.end());
+    P->irrep_tab.insert(P->irrep_tab.end(), ms.begin(), ms.end());
+    P->irrep_tab.insert(P->irrep_tab.end(), os.begin(), os.end());
+  }
 
   P->host_only = (flags & CGTP_PLAN_HOST_ONLY) != 0;
   if (!P->host_only) {
@@ -444,11 +494,19 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
       return fail(CGTP_ERR_NO_DEVICE, "current device is not gfx950");
     }
     P->device = dev;
-    const size_t jb = P->jobs.size() * sizeof(Job);
-    hipError_t e = hipMalloc(&P->d_tables, jb);
+    const size_t jb = align256(P->jobs.size() * sizeof(Job));
+    const size_t pb = align256(P->pdev.size() * sizeof(PathDev));
+    const size_t ib = P->irrep_tab.size() * sizeof(int32_t);
+    hipError_t e = hipMalloc(&P->d_tables, jb + pb + ib);
     if (e == hipSuccess) {
-      P->d_jobs = static_cast<Job*>(P->d_tables);
-      e = hipMemcpy(P->d_jobs, P->jobs.data(), jb, hipMemcpyHostToDevice);
+      char* base = static_cast<char*>(P->d_tables);
+      P->d_jobs = reinterpret_cast<Job*>(base);
+      P->d_paths = reinterpret_cast<PathDev*>(base + jb);
+      P->d_irrep = reinterpret_cast<int32_t*>(base + jb + pb);
+      e = hipMemcpy(P->d_jobs, P->jobs.data(), P->jobs.size() * sizeof(Job), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(P->d_paths, P->pdev.data(), P->pdev.size() * sizeof(PathDev), hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipMemcpy(P->d_irrep, P->irrep_tab.data(), ib, hipMemcpyHostToDevice);
     }
     if (e != hipSuccess) {
       if (P->d_tables) (void)hipFree(P->d_tables);
@@ -763,6 +821,132 @@ int cgtp_conv_forward_f64(cgtp_plan_t P, const double* pos, int64_t n_nodes, con
   return conv_forward_impl<double>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out, workspace,
                            ws_bytes, stream, static_cast<hipEvent_t>(ev_conv_begin),
                            static_cast<hipEvent_t>(ev_conv_end));
+}
+
+}  // extern "C"
+
+// Workspace of the backward: the forward's sections, then the sender-grouped slots, the
+// per-path dL/dY partials and dL/dr per slot.
+struct BwdWorkspace {
+  FwdWorkspace fwd;
+  int32_t *t_cnt, *t_row_ptr, *t_slot, *t_recv;
+  float *gyp, *grad_r;
+  size_t bytes;
+};
+
+static BwdWorkspace carve_bwd(const cgtp_plan_s& P, int64_t n, int64_t e, void* base) {
+  BwdWorkspace w{};
+  w.fwd = carve(P, n, e, base);
+  char* p = static_cast<char*>(base);
+  size_t off = w.fwd.bytes;
+  auto take = [&](size_t bytes) {
+    char* r = p ? p + off : nullptr;
+    off += align256(bytes);
+    return r;
+  };
+  w.t_cnt = reinterpret_cast<int32_t*>(take(size_t(n) * 4));
+  w.t_row_ptr = reinterpret_cast<int32_t*>(take(size_t(n + 1) * 4));
+  w.t_slot = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
+  w.t_recv = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
+  w.gyp = reinterpret_cast<float*>(take(size_t(e) * size_t(P.gy_stride) * 4));
+  w.grad_r = reinterpret_cast<float*>(take(size_t(e) * 12));
+  w.bytes = off;
+  return w;
+}
+
+extern "C" {
+
+int cgtp_backward_workspace_size(cgtp_plan_t P, int64_t n_nodes, int64_t n_edges, size_t* bytes) {
+  if (!P || !bytes) return fail(CGTP_ERR_INVALID_ARG, "NULL argument");
+  if (n_nodes < 0 || n_edges < 0) return fail(CGTP_ERR_INVALID_ARG, "negative size");
+  *bytes = carve_bwd(*P, n_nodes, n_edges, nullptr).bytes;
+  return ok();
+}
+
+int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9], const int32_t* row_ptr,
+                       const int32_t* col, const int8_t* shift, int64_t n_edges, const float* x, const float* w,
+                       const uint8_t* mask, const float* gate, const float* grad_out, float* grad_x, float* grad_w,
+                       float* grad_pos, void* workspace, size_t ws_bytes, void* stream) {
+  int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
+  if (rc != CGTP_OK) return rc;
+  if (P->elem != 4) return fail(CGTP_ERR_INVALID_ARG, "the backward is fp32: the plan's precision is fp64");
+  if (P->lmax > 3) return fail(CGTP_ERR_UNSUPPORTED, "the backward supports plans with l <= 3 (this one reaches %d)", P->lmax);
+  const bool any = grad_x || grad_w || grad_pos;
+  if (n_nodes > 0 && any && (!grad_out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
+  if (n_edges > 0 && any && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
+  if (!aligned(x, 4) || !aligned(w, 4) || !aligned(pos, 4) || !aligned(col, 4) || !aligned(gate, 4) ||
+      !aligned(grad_out, 4) || !aligned(grad_x, 4) || !aligned(grad_w, 4) || !aligned(grad_pos, 4))
+    return fail(CGTP_ERR_INVALID_ARG, "misaligned pointer");
+  const BwdWorkspace ws = carve_bwd(*P, n_nodes, n_edges, workspace);
+  if (!workspace || ws_bytes < ws.bytes)
+    return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, ws.bytes);
+  if (!aligned(workspace, 256)) return fail(CGTP_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (n_nodes == 0 || !any) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // 1. the forward's per-row pass: active slots, senders and gate-scaled harmonics
+  RowPass g{};
+  g.pos = pos;
+  g.row_ptr = row_ptr;
+  g.col = col;
+  g.shift = shift;
+  g.mask = mask;
+  g.gate = gate;
+  g.deg = ws.fwd.deg;
+  g.act_e = ws.fwd.act_e;
+  g.act_j = ws.fwd.act_j;
+  g.sh = static_cast<float*>(ws.fwd.sh);
+  g.sh_stride = P->sh_pad;
+  g.n_nodes = int(n_nodes);
+  g.n_edges = int(n_edges);
+  fill_cell(g, cell);
+  CGTP_HIP(launch_rows(g, P->l_sh_max, s));
+  BwdArgs a{};
+  a.x = x;
+  a.w = w;
+  a.sh = static_cast<const float*>(ws.fwd.sh);
+  a.grad_out = grad_out;
+  a.pos = pos;
+  a.row_ptr = row_ptr;
+  a.shift = shift;
+  a.mask = mask;
+  a.gate = gate;
+  a.deg = ws.fwd.deg;
+  a.act_e = ws.fwd.act_e;
+  a.act_j = ws.fwd.act_j;
+  a.paths = P->d_paths;
+  const int ni = int(P->in.size()), np = int(P->paths.size());
+  a.irrep_start = P->d_irrep;
+  a.irrep_paths = P->d_irrep + ni + 1;
+  a.irrep_l = P->d_irrep + ni + 1 + np;
+  a.irrep_mul = a.irrep_l + ni;
+  a.irrep_off = a.irrep_mul + ni;
+  a.t_row_ptr = ws.t_row_ptr;
+  a.t_slot = ws.t_slot;
+  a.t_recv = ws.t_recv;
+  a.grad_x = grad_x;
+  a.grad_w = grad_w;
+  a.gyp = ws.gyp;
+  a.grad_r = ws.grad_r;
+  a.grad_pos = grad_pos;
+  a.n_nodes = int(n_nodes);
+  a.n_paths = np;
+  a.n_irreps = ni;
+  a.f_in = int(P->f_in);
+  a.f_out = int(P->f_out);
+  a.w_stride = int(P->w);
+  a.sh_stride = P->sh_pad;
+  a.gy_stride = P->gy_stride;
+  a.l_sh_max = P->l_sh_max;
+  a.want_gy = grad_pos != nullptr;
+  a.has_cell = cell != nullptr;
+  for (int k = 0; k < 9; ++k) a.cell[k] = cell ? double(cell[k]) : 0.0;
+  // 2. w-gradient and the per-path dL/dY partials (receiver-major)
+  if (grad_w || grad_pos) CGTP_HIP(launch_bwd_edges(a, s));
+  // 3. active slots grouped by sender, then the x-gradient and the forces
+  if (grad_x || grad_pos) CGTP_HIP(launch_bwd_transpose(a, ws.t_cnt, ws.t_row_ptr, ws.t_slot, ws.t_recv, s));
+  if (grad_x) CGTP_HIP(launch_bwd_x(a, s));
+  if (grad_pos) CGTP_HIP(launch_bwd_pos(a, s));
+  return ok();
 }
 
 int cgtp_conv_forward_timed(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],

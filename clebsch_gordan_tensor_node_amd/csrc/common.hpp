@@ -87,6 +87,53 @@ using ConvArgs = ConvArgsT<float>;
 // the kernel classes (l <= 3) that are also built in fp64
 constexpr int kNumClassesF64 = 2;
 
+// One path of a plan, for the backward kernels (device table owned by the plan).
+struct PathDev {
+  int32_t variant;     // variant_index(l1, l2, l3, K = 1)
+  int32_t l1, l2, l3;
+  int32_t mul;
+  int32_t in_off, out_off, w_off;
+  int32_t sh_off;      // l2 * l2: the path's harmonics within an SH row
+  int32_t gy_off;      // the path's block within a row of per-path dL/dY partials
+  int32_t i_in;        // input irrep index
+  int32_t pad;
+};
+
+// Arguments of the backward kernels (fp32).  Active slots are those of the forward's
+// per-row pass: slot row_ptr[i] + q for the q-th active edge of row i.
+struct BwdArgs {
+  const float* x;
+  const float* w;
+  const float* sh;            // gate-scaled harmonics per active slot, rows of sh_stride
+  const float* grad_out;
+  const float* pos;
+  const int32_t* row_ptr;
+  const int8_t* shift;
+  const uint8_t* mask;
+  const float* gate;
+  const int32_t* deg;         // active edges per row
+  const int32_t* act_e;       // edge id per active slot
+  const int32_t* act_j;       // sender per active slot
+  const PathDev* paths;
+  const int32_t* irrep_start; // paths of input irrep a: irrep_paths[irrep_start[a] .. irrep_start[a+1])
+  const int32_t* irrep_paths;
+  const int32_t* irrep_l;     // per input irrep: l, multiplicity, offset in x
+  const int32_t* irrep_mul;
+  const int32_t* irrep_off;
+  const int32_t* t_row_ptr;   // active slots grouped by sender
+  const int32_t* t_slot;
+  const int32_t* t_recv;
+  float* grad_x;
+  float* grad_w;
+  float* gyp;                 // [slot, gy_stride] per-path dL/dY partials
+  float* grad_r;              // [slot, 3] dL/dr
+  float* grad_pos;
+  int32_t n_nodes, n_paths, n_irreps;
+  int32_t f_in, f_out, w_stride, sh_stride, gy_stride, l_sh_max;
+  int32_t want_gy, has_cell;
+  double cell[9];
+};
+
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 }  // namespace cgtp

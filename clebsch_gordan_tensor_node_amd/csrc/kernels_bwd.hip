@@ -1,0 +1,452 @@
+// Backward of the CGTP convolution (fp32, plans whose largest l is 3 or less).
+//
+// LunaTP's abstract puts the derivatives that forces need within the scope of its
+// kernels.  The forward is trilinear in (x_j, w_e, Y(r_e)), so with dL/d out = g:
+//   dL/dw[e, c]      = sum C x_j Y g_i             (one value per edge and channel)
+//   dL/dx[j, u, m1] += w sum_{m2,m3} C Y g_i        (summed over the sender's edges)
+//   dL/dY[e, m2]    += w sum_{m1,m3} C x_j g_i      (summed over paths and channels)
+//   dL/dr_e          = gate_e sum_m2 dL/dY[e, m2] dY_m2/dr,   dL/dpos = +dL/dr at the
+//                      sender, -dL/dr at the receiver.
+// The harmonics used are the forward's stored ones (already scaled by the gate), so the
+// w and x gradients carry the gate; dL/dY is taken with respect to the stored values,
+// hence the gate factor in dL/dr.
+//
+// gfx950 mapping: every pass is deterministic (no floating-point atomics; every sum runs
+// in a fixed order), and each path's coupling is a compile-time specialisation (the real
+// CG coefficients and their sparsity are constants):
+//   * bwd_edge_kernel: one wave per (receiver, path), lanes over channels; it walks the
+//     row's edges in CSR order, writes the w-gradient row segment of every edge (zeros
+//     for inactive ones) and reduces dL/dY over the lanes with a fixed butterfly;
+//   * the active slots are regrouped by sender (counts, scan, placement, per-sender sort
+//     by slot), so that the x-gradient is a gather: bwd_x_kernel runs one wave per
+//     (sender, input irrep) and accumulates all of that irrep's paths in registers;
+//   * bwd_force_kernel evaluates dY/dr by running the harmonics' recurrence on dual
+//     numbers (exact derivatives of the same polynomials), and bwd_pos_kernel sums each
+//     node's +/- contributions in slot order.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "sh_eval.hpp"
+#include "variants.hpp"
+
+namespace cgtp {
+
+namespace {
+
+constexpr int kBwdLmax = 3;
+
+template <int N>
+struct IC {
+  static constexpr int value = N;
+};
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    sfor<B + 1, E>(f);
+  }
+}
+
+template <int L1, int L2, int L3>
+inline constexpr RealCG<L1, L2, L3> kCGb{};
+
+// Runs f(IC<v>) for the variant v of a path: the scalar (K = 1) form of a triple with
+// l <= 3 (the kernels here specialise on (l1, l2, l3) only).
+template <int LO, int HI, typename F>
+__device__ __forceinline__ void by_variant(int v, F&& f) {
+  if constexpr (HI - LO == 1) {
+    if constexpr (variant_lmax(LO) <= kBwdLmax && variant_desc(LO).k == 1) f(IC<LO>{});
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (v < MID)
+      by_variant<LO, MID>(v, f);
+    else
+      by_variant<MID, HI>(v, f);
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ bool edge_active(const BwdArgs& a, int e) {
+  return (!a.mask || a.mask[e] != 0) && (!a.gate || a.gate[e] != 0.0f);
+}
+
+// A[m1][m3] = sum_m2 C[m1,m2,m3] Y[m2]
+template <int L1, int L2, int L3>
+__device__ __forceinline__ void form_a(const float* Y, float (*A)[2 * L3 + 1]) {
+  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
+  sfor<0, N1>([&](auto M1) {
+    sfor<0, N3>([&](auto M3) {
+      float s = 0.0f;
+      sfor<0, N2>([&](auto M2) {
+        constexpr float c = kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
+        if constexpr (c != 0.0f) s = __builtin_fmaf(c, Y[decltype(M2)::value], s);
+      });
+      A[decltype(M1)::value][decltype(M3)::value] = s;
+    });
+  });
+}
+
+// ---------------------------------------------------------------------------------
+// w-gradient and per-path dL/dY
+// ---------------------------------------------------------------------------------
+
+template <int L1, int L2, int L3>
+__device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P, int i) {
+  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
+  const int lane = int(threadIdx.x);
+  const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
+  const bool gy_on = a.want_gy && L2 > 0;
+  int q = 0;
+  for (int e = rb; e < re; ++e) {
+    if (!edge_active(a, e)) {
+      if (a.grad_w)
+        for (int u = lane; u < P.mul; u += kWave) a.grad_w[(long)e * a.w_stride + P.w_off + u] = 0.0f;
+      continue;
+    }
+    const int s = rb + q++;
+    const int j = a.act_j[s];
+    float Y[N2];
+#pragma unroll
+    for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
+    float A[N1][N3];
+    form_a<L1, L2, L3>(Y, A);
+    float gy[N2];
+#pragma unroll
+    for (int m = 0; m < N2; ++m) gy[m] = 0.0f;
+    for (int u = lane; u < P.mul; u += kWave) {
+      float xv[N1], go[N3];
+#pragma unroll
+      for (int m = 0; m < N1; ++m) xv[m] = a.x[(long)j * a.f_in + P.in_off + u * N1 + m];
+#pragma unroll
+      for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + u * N3 + m];
+      if (a.grad_w) {
+        float gw = 0.0f;
+#pragma unroll
+        for (int m3 = 0; m3 < N3; ++m3) {
+          float t = 0.0f;
+#pragma unroll
+          for (int m1 = 0; m1 < N1; ++m1) t = __builtin_fmaf(A[m1][m3], xv[m1], t);
+          gw = __builtin_fmaf(t, go[m3], gw);
+        }
+        a.grad_w[(long)e * a.w_stride + P.w_off + u] = gw;
+      }
+      if (gy_on) {
+        const float wv = a.w[(long)e * a.w_stride + P.w_off + u];
+#pragma unroll
+        for (int m = 0; m < N1; ++m) xv[m] *= wv;
+        sfor<0, N1>([&](auto M1) {
+          sfor<0, N2>([&](auto M2) {
+            sfor<0, N3>([&](auto M3) {
+              constexpr float c =
+                  kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
+              if constexpr (c != 0.0f)
+                gy[decltype(M2)::value] =
+                    __builtin_fmaf(c * xv[decltype(M1)::value], go[decltype(M3)::value], gy[decltype(M2)::value]);
+            });
+          });
+        });
+      }
+    }
+    if (gy_on) {
+#pragma unroll
+      for (int m = 0; m < N2; ++m) {
+        const float v = wave_sum(gy[m]);
+        if (lane == 0) a.gyp[(long)s * a.gy_stride + P.gy_off + m] = v;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kWave) bwd_edge_kernel(BwdArgs a) {
+  const int i = int(blockIdx.x);
+  const PathDev P = a.paths[blockIdx.y];
+  by_variant<0, kNumVariants>(P.variant, [&](auto V) {
+    constexpr VariantDesc d = variant_desc(decltype(V)::value);
+    bwd_edge_path<d.l1, d.l2, d.l3>(a, P, i);
+  });
+}
+
+// ---------------------------------------------------------------------------------
+// active slots grouped by sender
+// ---------------------------------------------------------------------------------
+
+__global__ void fill_zero_kernel(int32_t* p, int n) {
+  const int k = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (k < n) p[k] = 0;
+}
+
+// one wave per row: count (place == 0) or place (place == 1) the row's active slots
+__global__ void __launch_bounds__(256) bwd_t_count_kernel(BwdArgs a, int32_t* cnt, int32_t* t_slot, int32_t* t_recv,
+                                                          int place) {
+  const int i = int(blockIdx.x) * (256 / kWave) + int(threadIdx.x) / kWave;
+  if (i >= a.n_nodes) return;
+  const int lane = int(threadIdx.x) & (kWave - 1);
+  const int rb = a.row_ptr[i], d = a.deg[i];
+  for (int q = lane; q < d; q += kWave) {
+    const int s = rb + q;
+    const int j = a.act_j[s];
+    const int k = atomicAdd(&cnt[j], 1);
+    if (place) {
+      t_slot[a.t_row_ptr[j] + k] = s;
+      t_recv[a.t_row_ptr[j] + k] = i;
+    }
+  }
+}
+
+// one workgroup: out[k] = sum_{q < k} in[q], k <= n
+__global__ void __launch_bounds__(1024) bwd_scan_kernel(const int32_t* in, int32_t* out, int n) {
+  __shared__ int wsum[1024 / kWave + 1];
+  const int lane = int(threadIdx.x) & (kWave - 1), wave = int(threadIdx.x) / kWave;
+  int carry = 0;
+  for (int base = 0; base < n; base += 1024) {
+    const int idx = base + int(threadIdx.x);
+    const int v = idx < n ? in[idx] : 0;
+    int inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(inc, d, kWave);
+      if (lane >= d) inc += t;
+    }
+    if (lane == kWave - 1) wsum[wave] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int run = 0;
+      for (int k = 0; k < 1024 / kWave; ++k) {
+        const int t = wsum[k];
+        wsum[k] = run;
+        run += t;
+      }
+      wsum[1024 / kWave] = run;
+    }
+    __syncthreads();
+    if (idx < n) out[idx] = carry + wsum[wave] + inc - v;
+    carry += wsum[1024 / kWave];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[n] = carry;
+}
+
+// one thread per sender: its entries in slot order (insertion sort; rows are short)
+__global__ void bwd_t_sort_kernel(const int32_t* t_row_ptr, int32_t* t_slot, int32_t* t_recv, int n) {
+  const int j = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (j >= n) return;
+  const int b = t_row_ptr[j], e = t_row_ptr[j + 1];
+  for (int k = b + 1; k < e; ++k) {
+    const int s = t_slot[k], r = t_recv[k];
+    int m = k - 1;
+    while (m >= b && t_slot[m] > s) {
+      t_slot[m + 1] = t_slot[m];
+      t_recv[m + 1] = t_recv[m];
+      --m;
+    }
+    t_slot[m + 1] = s;
+    t_recv[m + 1] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// x-gradient
+// ---------------------------------------------------------------------------------
+
+template <int L1, int L2, int L3>
+__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int j, int u, bool ok, float* acc) {
+  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
+  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
+  for (int k = tb; k < te; ++k) {
+    const int s = a.t_slot[k], i = a.t_recv[k];
+    float Y[N2];
+#pragma unroll
+    for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
+    float A[N1][N3];
+    form_a<L1, L2, L3>(Y, A);
+    if (ok) {
+      const float wv = a.w[(long)a.act_e[s] * a.w_stride + P.w_off + u];
+      float go[N3];
+#pragma unroll
+      for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + u * N3 + m];
+#pragma unroll
+      for (int m1 = 0; m1 < N1; ++m1) {
+        float t = 0.0f;
+#pragma unroll
+        for (int m3 = 0; m3 < N3; ++m3) t = __builtin_fmaf(A[m1][m3], go[m3], t);
+        acc[m1] = __builtin_fmaf(wv, t, acc[m1]);
+      }
+    }
+  }
+}
+
+template <int L1>
+__device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
+  constexpr int N1 = 2 * L1 + 1;
+  const int mul = a.irrep_mul[ir], off = a.irrep_off[ir];
+  const int p0 = a.irrep_start[ir], p1 = a.irrep_start[ir + 1];
+  for (int u0 = 0; u0 < mul; u0 += kWave) {
+    const int u = u0 + int(threadIdx.x);
+    const bool ok = u < mul;
+    float acc[N1];
+#pragma unroll
+    for (int m = 0; m < N1; ++m) acc[m] = 0.0f;
+    for (int pp = p0; pp < p1; ++pp) {
+      const PathDev P = a.paths[a.irrep_paths[pp]];
+      by_variant<0, kNumVariants>(P.variant, [&](auto V) {
+        constexpr VariantDesc d = variant_desc(decltype(V)::value);
+        if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, j, u, ok, acc);
+      });
+    }
+    if (ok) {
+#pragma unroll
+      for (int m = 0; m < N1; ++m) a.grad_x[(long)j * a.f_in + off + u * N1 + m] = acc[m];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kWave) bwd_x_kernel(BwdArgs a) {
+  const int j = int(blockIdx.x), ir = int(blockIdx.y);
+  switch (a.irrep_l[ir]) {
+    case 0: bwd_x_irrep<0>(a, j, ir); break;
+    case 1: bwd_x_irrep<1>(a, j, ir); break;
+    case 2: bwd_x_irrep<2>(a, j, ir); break;
+    case 3: bwd_x_irrep<3>(a, j, ir); break;
+    default: break;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// dL/dr per active slot, and the position gradient
+// ---------------------------------------------------------------------------------
+
+template <int L>
+__device__ __forceinline__ void slot_grad_r(const BwdArgs& a, int i, int s) {
+  constexpr int NY = (L + 1) * (L + 1);
+  // dL/dY of the slot: the paths' partials in path order
+  float g[NY];
+#pragma unroll
+  for (int k = 0; k < NY; ++k) g[k] = 0.0f;
+  for (int p = 0; p < a.n_paths; ++p) {
+    const PathDev P = a.paths[p];
+    sfor<1, L + 1>([&](auto L2c) {
+      constexpr int L2 = decltype(L2c)::value;
+      if (P.l2 == L2) {
+#pragma unroll
+        for (int m = 0; m < 2 * L2 + 1; ++m) g[L2 * L2 + m] += a.gyp[(long)s * a.gy_stride + P.gy_off + m];
+      }
+    });
+  }
+  const int e = a.act_e[s], j = a.act_j[s];
+  double r[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) r[k] = double(a.pos[3 * j + k]) - double(a.pos[3 * i + k]);
+  if (a.has_cell && a.shift) {
+    const double s0 = a.shift[3 * e + 0], s1 = a.shift[3 * e + 1], s2 = a.shift[3 * e + 2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) r[k] = r[k] + s0 * a.cell[k] + s1 * a.cell[3 + k] + s2 * a.cell[6 + k];
+  }
+  const double rr = sqrt(r[0] * r[0] + r[1] * r[1] + r[2] * r[2]);
+  double gr[3] = {0.0, 0.0, 0.0};
+  if (rr > 0.0) {   // a zero-length edge has constant harmonics: no gradient
+    const double inv = 1.0 / rr;
+    const double rh[3] = {r[0] * inv, r[1] * inv, r[2] * inv};
+    // the unit vector's components with d rhat_a / d r_k = (delta_ak - rhat_a rhat_k) / |r|
+    Dual3 u[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      u[c] = Dual3(rh[c]);
+#pragma unroll
+      for (int k = 0; k < 3; ++k) u[c].d[k] = ((c == k ? 1.0 : 0.0) - rh[c] * rh[k]) * inv;
+    }
+    Dual3 Y[NY];
+    sh_unit<L, Dual3>(u[0], u[1], u[2], Y);
+    const double gt = a.gate ? double(a.gate[e]) : 1.0;
+#pragma unroll
+    for (int q = 1; q < NY; ++q)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) gr[k] += double(g[q]) * Y[q].d[k];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) gr[k] *= gt;
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) a.grad_r[(long)s * 3 + k] = float(gr[k]);
+}
+
+// one wave per row, lanes over its active slots
+__global__ void __launch_bounds__(256) bwd_force_kernel(BwdArgs a) {
+  const int i = int(blockIdx.x) * (256 / kWave) + int(threadIdx.x) / kWave;
+  if (i >= a.n_nodes) return;
+  const int lane = int(threadIdx.x) & (kWave - 1);
+  const int rb = a.row_ptr[i], d = a.deg[i];
+  for (int q = lane; q < d; q += kWave) {
+    switch (a.l_sh_max) {
+      case 1: slot_grad_r<1>(a, i, rb + q); break;
+      case 2: slot_grad_r<2>(a, i, rb + q); break;
+      case 3: slot_grad_r<3>(a, i, rb + q); break;
+      default:   // l = 0 harmonics only: constant, no gradient
+#pragma unroll
+        for (int k = 0; k < 3; ++k) a.grad_r[(long)(rb + q) * 3 + k] = 0.0f;
+        break;
+    }
+  }
+}
+
+// one thread per node: + its edges as sender, - its edges as receiver, in slot order
+__global__ void bwd_pos_kernel(BwdArgs a) {
+  const int n = int(blockIdx.x * blockDim.x + threadIdx.x);
+  if (n >= a.n_nodes) return;
+  double g[3] = {0.0, 0.0, 0.0};
+  for (int k = a.t_row_ptr[n]; k < a.t_row_ptr[n + 1]; ++k) {
+    const int s = a.t_slot[k];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g[c] += double(a.grad_r[(long)s * 3 + c]);
+  }
+  const int rb = a.row_ptr[n], d = a.deg[n];
+  for (int q = 0; q < d; ++q)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g[c] -= double(a.grad_r[(long)(rb + q) * 3 + c]);
+#pragma unroll
+  for (int c = 0; c < 3; ++c) a.grad_pos[3 * n + c] = float(g[c]);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_edges(const BwdArgs& a, hipStream_t s) {
+  if (a.n_nodes == 0 || a.n_paths == 0) return hipSuccess;
+  bwd_edge_kernel<<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,
+                                int32_t* t_recv, hipStream_t s) {
+  const int n = a.n_nodes;
+  if (n == 0) return hipSuccess;
+  const int zb = ceil_div(n, 256), rb = ceil_div(n, 256 / kWave);
+  fill_zero_kernel<<<zb, 256, 0, s>>>(t_cnt, n);
+  bwd_t_count_kernel<<<rb, 256, 0, s>>>(a, t_cnt, nullptr, nullptr, 0);
+  bwd_scan_kernel<<<1, 1024, 0, s>>>(t_cnt, t_row_ptr, n);
+  fill_zero_kernel<<<zb, 256, 0, s>>>(t_cnt, n);
+  BwdArgs b = a;
+  b.t_row_ptr = t_row_ptr;
+  bwd_t_count_kernel<<<rb, 256, 0, s>>>(b, t_cnt, t_slot, t_recv, 1);
+  bwd_t_sort_kernel<<<zb, 256, 0, s>>>(t_row_ptr, t_slot, t_recv, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_x(const BwdArgs& a, hipStream_t s) {
+  if (a.n_nodes == 0 || a.n_irreps == 0) return hipSuccess;
+  bwd_x_kernel<<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s) {
+  const int n = a.n_nodes;
+  if (n == 0) return hipSuccess;
+  bwd_force_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
+  bwd_pos_kernel<<<ceil_div(n, 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace cgtp

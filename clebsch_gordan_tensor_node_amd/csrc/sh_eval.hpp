@@ -35,26 +35,61 @@ struct ShConst {
   }
 };
 
-// Y[(L+1)^2], index l*l + l + m, for the unit vector (x, y, z).
-template <int L>
-__host__ __device__ inline void sh_unit(double x, double y, double z, double* Y) {
+// A value and its derivatives with respect to the three components of an edge vector
+// (forward-mode differentiation): running the harmonics' recurrence on these gives
+// dY/dr exactly, through the same polynomial arithmetic as Y itself.
+struct Dual3 {
+  double v, d[3];
+  __host__ __device__ Dual3() : v(0.0), d{0.0, 0.0, 0.0} {}
+  __host__ __device__ Dual3(double c) : v(c), d{0.0, 0.0, 0.0} {}
+};
+__host__ __device__ inline Dual3 operator+(const Dual3& a, const Dual3& b) {
+  Dual3 r(a.v + b.v);
+  for (int k = 0; k < 3; ++k) r.d[k] = a.d[k] + b.d[k];
+  return r;
+}
+__host__ __device__ inline Dual3 operator-(const Dual3& a, const Dual3& b) {
+  Dual3 r(a.v - b.v);
+  for (int k = 0; k < 3; ++k) r.d[k] = a.d[k] - b.d[k];
+  return r;
+}
+__host__ __device__ inline Dual3 operator*(const Dual3& a, const Dual3& b) {
+  Dual3 r(a.v * b.v);
+  for (int k = 0; k < 3; ++k) r.d[k] = a.d[k] * b.v + a.v * b.d[k];
+  return r;
+}
+__host__ __device__ inline Dual3 operator*(double c, const Dual3& a) {
+  Dual3 r(c * a.v);
+  for (int k = 0; k < 3; ++k) r.d[k] = c * a.d[k];
+  return r;
+}
+__host__ __device__ inline Dual3 operator/(const Dual3& a, double c) {
+  Dual3 r(a.v / c);
+  for (int k = 0; k < 3; ++k) r.d[k] = a.d[k] / c;
+  return r;
+}
+
+// Y[(L+1)^2], index l*l + l + m, for the unit vector (x, y, z); S = double, or Dual3
+// for the harmonics together with their derivatives.
+template <int L, typename S = double>
+__host__ __device__ inline void sh_unit(S x, S y, S z, S* Y) {
   constexpr ShConst K{};
-  double C[L + 1], S[L + 1];
-  C[0] = 1.0;
-  S[0] = 0.0;
+  S C[L + 1], Sn[L + 1];
+  C[0] = S(1.0);
+  Sn[0] = S(0.0);
 #pragma unroll
   for (int m = 1; m <= L; ++m) {
-    C[m] = x * C[m - 1] - y * S[m - 1];
-    S[m] = x * S[m - 1] + y * C[m - 1];
+    C[m] = x * C[m - 1] - y * Sn[m - 1];
+    Sn[m] = x * Sn[m - 1] + y * C[m - 1];
   }
 #pragma unroll
   for (int m = 0; m <= L; ++m) {
-    double q2 = 0.0, q1 = 0.0;
+    S q2(0.0), q1(0.0);
 #pragma unroll
     for (int l = m; l <= L; ++l) {
-      double q;
+      S q;
       if (l == m)
-        q = K.qmm[m];
+        q = S(K.qmm[m]);
       else if (l == m + 1)
         q = double(2 * m + 1) * z * q1;
       else
@@ -65,7 +100,7 @@ __host__ __device__ inline void sh_unit(double x, double y, double z, double* Y)
         Y[l * l + l] = K.norm[l][0] * q;
       } else {
         Y[l * l + l + m] = K.norm[l][m] * q * C[m];
-        Y[l * l + l - m] = K.norm[l][m] * q * S[m];
+        Y[l * l + l - m] = K.norm[l][m] * q * Sn[m];
       }
     }
   }

@@ -1,6 +1,7 @@
 /*
  * cgtp.h -- C ABI of libcgtp.so: the Clebsch-Gordan tensor-product (CGTP)
- * convolution, forward (fp32, and fp64 for l <= 3), for AMD Instinct MI355X (gfx950).
+ * convolution, forward (fp32, and fp64 for l <= 3) and gradients (fp32, l <= 3), for
+ * AMD Instinct MI355X (gfx950).
  *
  * What is computed (the pages print no formula; this is the textbook definition that
  * LunaTP's abstract says its kernels preserve):
@@ -194,6 +195,30 @@ int cgtp_conv_forward_f64(cgtp_plan_t plan, const double* pos, int64_t n_nodes, 
                           int64_t n_edges, const double* x, const double* w, const uint8_t* mask,
                           const double* gate, double* out, void* workspace, size_t ws_bytes,
                           void* stream, void* ev_conv_begin, void* ev_conv_end);
+
+/* Workspace bytes that cgtp_conv_backward needs for this graph size (alignment 256). */
+int cgtp_backward_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes);
+
+/* Gradients of the convolution (the backward pass; LunaTP, Abstract: the derivatives
+ * that forces need are within its kernels' scope).  Given grad_out = dL/d out
+ * [n_nodes, f_out] for a scalar L of the forward's output, writes (each may be NULL to
+ * skip it; each is overwritten):
+ *   grad_x [n_nodes, f_in]:   dL/dx;
+ *   grad_w [n_edges, w_per_edge]: dL/dw, rows of inactive edges exactly 0;
+ *   grad_pos [n_nodes, 3]:    dL/dpos through r_e = pos[j] - pos[i] + shift_e . cell and
+ *                             dY/dr (forces are -grad_pos when L is an energy).
+ * The mask, gate (BranchIP continuation gate; it scales the message and is not
+ * differentiated), cell and shifts are constants; inactive edges contribute nothing
+ * and their w and x_j are never read.  fp32 plans whose largest l is 3 or less (else
+ * CGTP_ERR_UNSUPPORTED; an fp64 plan gives CGTP_ERR_INVALID_ARG).  Other arguments as
+ * cgtp_conv_forward_gated; 4-byte aligned pointers; workspace at least
+ * cgtp_backward_workspace_size.  Asynchronous on `stream`; results are bitwise
+ * reproducible (no floating-point atomics). */
+int cgtp_conv_backward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
+                       const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
+                       int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
+                       const float* gate, const float* grad_out, float* grad_x, float* grad_w,
+                       float* grad_pos, void* workspace, size_t ws_bytes, void* stream);
 
 void cgtp_plan_destroy(cgtp_plan_t plan);
 
