@@ -2,6 +2,7 @@
 """Benchmark of the CGTP convolution forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1_768] [--dtype f32|f64]
+                    [--pass fwd|bwd]
 
 One step = one pass of the hot path over resident inputs: mask prepare (active CSR and
 degree order), per-edge compaction and harmonics, and the fused convolution kernel(s).
@@ -97,6 +98,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="c1_768")
     ap.add_argument("--dtype", choices=["f32", "f64"], default="f32",
                     help="arithmetic type of the forward (f64: plans with l <= 3)")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="bwd: time the backward step (x, w and position gradients; fp32, l <= 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-warm-cache", action="store_true",
@@ -171,6 +174,9 @@ def main(argv=None) -> int:
     wbufs = [w0] + [w0.clone() for _ in range(k - 1)]
     outs = [torch.empty((n, plan.f_out), dtype=plan.dtype, device=dev) for _ in range(k)]
     ws = torch.empty(plan.workspace_size(n, e, mask is not None), dtype=torch.uint8, device=dev)
+    if a.which == "bwd":
+        return bench_backward(a, C, wl, plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs, mask_d, gate_d,
+                              n, e, e_act, k, t_nbr)
 
     def step(s, evs=None):
         C.conv_forward(plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs[s % k], mask_d, out=outs[s % k],
@@ -259,6 +265,106 @@ def main(argv=None) -> int:
         out["cpu_baseline"] = cpu_baseline(wl, a.cpu_seconds)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def bench_backward(a, C, wl, plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs, mask_d, gate_d, n, e, e_act, k,
+                   t_nbr):
+    """K backward steps (x, w and position gradients) over rotated weight and gradient
+    buffers; the roofline is taken over the whole step (every backward kernel)."""
+    import numpy as np
+    import torch
+
+    dev = pos_d.device
+    rng = np.random.default_rng(1234)
+    g0 = torch.from_numpy(rng.standard_normal((n, plan.f_out)).astype(np.float32)).to(dev)
+    gouts = [g0] + [g0.clone() for _ in range(k - 1)]
+    gws = [torch.empty_like(wbufs[0]) for _ in range(k)]
+    gx = torch.empty((n, plan.f_in), dtype=torch.float32, device=dev)
+    gp = torch.empty((n, 3), dtype=torch.float32, device=dev)
+    ws = torch.empty(plan.backward_workspace_size(n, e), dtype=torch.uint8, device=dev)
+    lib = C._lib.load()
+    cella = None if cell is None else np.ascontiguousarray(np.asarray(cell, dtype=np.float32).reshape(-1))
+    cellp = None if cella is None else cella.ctypes.data_as(C._lib.FP)
+    P = lambda t: None if t is None else __import__("ctypes").c_void_p(t.data_ptr())
+
+    def step(s):
+        stream = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
+        C.check(lib.cgtp_conv_backward(plan.handle, P(pos_d), n, cellp, P(row_ptr), P(col), P(shift), e,
+                                       P(x_d), P(wbufs[s % k]), P(mask_d), P(gate_d), P(gouts[s % k]), P(gx),
+                                       P(gws[s % k]), P(gp), P(ws), ws.numel(), stream))
+
+    K, W = a.steps, a.warmup
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_beg.record()
+    for s in range(K):
+        step(W + s)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_beg.elapsed_time(t_end) / K
+    # algorithmic bytes of the backward, each moved once: w of the active edges and the
+    # w-gradient of every edge (4 W each), the edge list (as the forward), x and
+    # grad_x (4 F_in per node each), grad_out (4 F_out per node), positions and their
+    # gradient (12 + 12 per node), row pointers
+    bwd_bytes = (4 * plan.w_per_edge * e_act + 4 * plan.w_per_edge * e
+                 + e * (4 + 3 + (1 if mask_d is not None else 0) + (4 if gate_d is not None else 0))
+                 + 4 * (n + 1) + 24 * n + 8 * plan.f_in * n + 4 * plan.f_out * n)
+    achieved = bwd_bytes / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "CGTP conv backward edges/sec on 1 MI355X; % of HBM roofline",
+        "value": e / (ms_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "pass": "backward (grad_x, grad_w, grad_pos)", "n_atoms": n,
+                   "n_edges": e, "n_active_edges": e_act, "irreps_in": wl.irreps_in, "irreps_sh": wl.irreps_sh,
+                   "paths": plan.n_paths, "masked": wl.masked, "gated": wl.gated},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "backward step (every backward kernel, per-kernel times in profiles/)",
+                     "kernel_ms": ms_step, "alg_bytes_per_launch": bwd_bytes},
+        "rotation_buffers": k,
+        "nbr_build_ms": 1e3 * float(np.median(t_nbr)),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(wl, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_backward(wl, min_seconds: float):
+    """The oracle's conv_backward as it stands, single-threaded, over whole workloads."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    import workloads as WL
+
+    pos, box, cell, rng = WL.positions(wl)
+    rp, col, sh = O.neighbors(pos, box, wl.cutoff)
+    plan = O.build_plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    x, w, mask = WL.draw_payload(wl, rng, wl.n_atoms, plan.f_in, len(col), plan.w_per_edge)
+    gate = WL.gate_values(wl, rng, len(col))
+    gout = np.random.default_rng(1234).standard_normal((wl.n_atoms, plan.f_out))
+    reps, spent = 0, 0.0
+    with threadpool_limits(1):
+        while reps == 0 or (spent < min_seconds and reps < 10):
+            t0 = time.perf_counter()
+            O.conv_backward(plan, pos, cell, rp, col, sh, x, w, gout, mask, gate)
+            spent += time.perf_counter() - t0
+            reps += 1
+    return {"value": len(col) * reps / spent, "unit": "edges/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole {wl.name} workload ({len(col)} edges), {reps} run(s), {spent:.1f} s, "
+                      f"numpy fp64 conv_backward, BLAS limited to 1 thread"}
 
 
 if __name__ == "__main__":

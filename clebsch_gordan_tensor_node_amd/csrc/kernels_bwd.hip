@@ -102,15 +102,27 @@ __device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P
   const int lane = int(threadIdx.x);
   const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
   const bool gy_on = a.want_gy && L2 > 0;
-  int q = 0;
-  for (int e = rb; e < re; ++e) {
-    if (!edge_active(a, e)) {
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int q0 = 0;
+  // the row's edges 64 at a time: activity, slot and sender of edge e0 + lane loaded
+  // once, in parallel, then broadcast edge by edge (no dependent load per edge)
+  for (int e0 = rb; e0 < re; e0 += kWave) {
+    const int my_e = e0 + lane;
+    const bool my_act = my_e < re && edge_active(a, my_e);
+    const unsigned long long bal = __ballot(my_act);
+    const int my_s = rb + q0 + __popcll(bal & lt);
+    const int my_j = my_act ? a.act_j[my_s] : 0;
+    q0 += __popcll(bal);
+    const int cnt = min(kWave, re - e0);
+  for (int k = 0; k < cnt; ++k) {
+    const int e = e0 + k;
+    if (!((bal >> k) & 1ull)) {
       if (a.grad_w)
         for (int u = lane; u < P.mul; u += kWave) a.grad_w[(long)e * a.w_stride + P.w_off + u] = 0.0f;
       continue;
     }
-    const int s = rb + q++;
-    const int j = a.act_j[s];
+    const int s = __shfl(my_s, k, kWave);
+    const int j = __shfl(my_j, k, kWave);
     float Y[N2];
 #pragma unroll
     for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
@@ -160,6 +172,7 @@ __device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P
         if (lane == 0) a.gyp[(long)s * a.gy_stride + P.gy_off + m] = v;
       }
     }
+  }
   }
 }
 
@@ -232,11 +245,33 @@ __global__ void __launch_bounds__(1024) bwd_scan_kernel(const int32_t* in, int32
   if (threadIdx.x == 0) out[n] = carry;
 }
 
-// one thread per sender: its entries in slot order (insertion sort; rows are short)
-__global__ void bwd_t_sort_kernel(const int32_t* t_row_ptr, int32_t* t_slot, int32_t* t_recv, int n) {
-  const int j = int(blockIdx.x * blockDim.x + threadIdx.x);
-  if (j >= n) return;
-  const int b = t_row_ptr[j], e = t_row_ptr[j + 1];
+// one wave per sender: its entries in slot order.  Slots are distinct, so an entry's
+// position is the number of entries with a smaller slot (counted over an LDS copy of
+// the row); rows longer than the LDS copy are sorted by insertion by one lane.
+constexpr int kSortCap = 512;
+__global__ void __launch_bounds__(kWave) bwd_t_sort_kernel(const int32_t* t_row_ptr, int32_t* t_slot,
+                                                          int32_t* t_recv, int n) {
+  __shared__ int ss[kSortCap], rr[kSortCap];
+  const int j = int(blockIdx.x);
+  const int lane = int(threadIdx.x);
+  const int b = t_row_ptr[j], e = t_row_ptr[j + 1], len = e - b;
+  if (len <= 1) return;
+  if (len <= kSortCap) {
+    for (int k = lane; k < len; k += kWave) {
+      ss[k] = t_slot[b + k];
+      rr[k] = t_recv[b + k];
+    }
+    __syncthreads();
+    for (int k = lane; k < len; k += kWave) {
+      const int v = ss[k];
+      int rank = 0;
+      for (int m = 0; m < len; ++m) rank += ss[m] < v ? 1 : 0;
+      t_slot[b + rank] = v;
+      t_recv[b + rank] = rr[k];
+    }
+    return;
+  }
+  if (lane != 0) return;
   for (int k = b + 1; k < e; ++k) {
     const int s = t_slot[k], r = t_recv[k];
     int m = k - 1;
@@ -254,19 +289,21 @@ __global__ void bwd_t_sort_kernel(const int32_t* t_row_ptr, int32_t* t_slot, int
 // x-gradient
 // ---------------------------------------------------------------------------------
 
+// entries k0 .. k0 + cnt - 1 of the sender's list: slot, receiver and edge id of entry
+// k0 + lane are held by that lane
 template <int L1, int L2, int L3>
-__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int j, int u, bool ok, float* acc) {
+__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int cnt, int my_s, int my_i,
+                                           int my_e, int u, bool ok, float* acc) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
-  for (int k = tb; k < te; ++k) {
-    const int s = a.t_slot[k], i = a.t_recv[k];
+  for (int k = 0; k < cnt; ++k) {
+    const int s = __shfl(my_s, k, kWave), i = __shfl(my_i, k, kWave), e = __shfl(my_e, k, kWave);
     float Y[N2];
 #pragma unroll
     for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
     float A[N1][N3];
     form_a<L1, L2, L3>(Y, A);
     if (ok) {
-      const float wv = a.w[(long)a.act_e[s] * a.w_stride + P.w_off + u];
+      const float wv = a.w[(long)e * a.w_stride + P.w_off + u];
       float go[N3];
 #pragma unroll
       for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + u * N3 + m];
@@ -292,12 +329,19 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
     float acc[N1];
 #pragma unroll
     for (int m = 0; m < N1; ++m) acc[m] = 0.0f;
-    for (int pp = p0; pp < p1; ++pp) {
-      const PathDev P = a.paths[a.irrep_paths[pp]];
-      by_variant<0, kNumVariants>(P.variant, [&](auto V) {
-        constexpr VariantDesc d = variant_desc(decltype(V)::value);
-        if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, j, u, ok, acc);
-      });
+    const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
+    for (int k0 = tb; k0 < te; k0 += kWave) {
+      const int cnt = min(kWave, te - k0);
+      const int kk = k0 + min(int(threadIdx.x), cnt - 1);
+      const int my_s = a.t_slot[kk], my_i = a.t_recv[kk];
+      const int my_e = a.act_e[my_s];
+      for (int pp = p0; pp < p1; ++pp) {
+        const PathDev P = a.paths[a.irrep_paths[pp]];
+        by_variant<0, kNumVariants>(P.variant, [&](auto V) {
+          constexpr VariantDesc d = variant_desc(decltype(V)::value);
+          if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, cnt, my_s, my_i, my_e, u, ok, acc);
+        });
+      }
     }
     if (ok) {
 #pragma unroll
@@ -431,7 +475,7 @@ hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row
   BwdArgs b = a;
   b.t_row_ptr = t_row_ptr;
   bwd_t_count_kernel<<<rb, 256, 0, s>>>(b, t_cnt, t_slot, t_recv, 1);
-  bwd_t_sort_kernel<<<zb, 256, 0, s>>>(t_row_ptr, t_slot, t_recv, n);
+  bwd_t_sort_kernel<<<n, kWave, 0, s>>>(t_row_ptr, t_slot, t_recv, n);
   return hipGetLastError();
 }
 
