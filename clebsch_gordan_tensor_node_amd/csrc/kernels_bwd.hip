@@ -14,9 +14,10 @@
 // gfx950 mapping: every pass is deterministic (no floating-point atomics; every sum runs
 // in a fixed order), and each path's coupling is a compile-time specialisation (the real
 // CG coefficients and their sparsity are constants):
-//   * bwd_edge_kernel: one wave per (receiver, path), lanes over channels; it walks the
-//     row's edges in CSR order, writes the w-gradient row segment of every edge (zeros
-//     for inactive ones) and reduces dL/dY over the lanes with a fixed butterfly;
+//   * bwd_edge_kernel: one wave per (receiver, path), lanes over channels; it lists the
+//     row's active edges in LDS, zeroes the w-gradient rows of the inactive ones, walks
+//     the active ones with a one-deep load pipeline, writes their w-gradient and reduces
+//     dL/dY over the lanes with a fixed butterfly;
 //   * the active slots are regrouped by sender (counts, scan, placement, per-sender sort
 //     by slot), so that the x-gradient is a gather: bwd_x_kernel runs one wave per
 //     (sender, input irrep) and accumulates all of that irrep's paths in registers;
@@ -96,92 +97,148 @@ __device__ __forceinline__ void form_a(const float* Y, float (*A)[2 * L3 + 1]) {
 // w-gradient and per-path dL/dY
 // ---------------------------------------------------------------------------------
 
+constexpr int kSeg = 256;      // active edges of a row listed in LDS at a time
+constexpr int kChunks = 2;     // channel chunks of 64 lanes held in registers (128 channels)
+
+struct EdgeLists {
+  int e[kSeg], s[kSeg], j[kSeg], z[kSeg];   // active: edge, slot, sender; inactive: edge
+};
+
+// One wave per (receiver i, path).  Per segment of the row: the active edges (edge id,
+// slot, sender) are compacted into LDS and the w-gradient rows of the inactive ones are
+// zeroed with coalesced stores; then the active edges are walked with a one-deep
+// pipeline: the next edge's harmonics, x_j and weights are loaded (unconditionally, at a
+// clamped index) while the current edge is computed.  Channels u = uc + 64 c + lane,
+// c < kChunks, with grad_out of the row held in registers.
 template <int L1, int L2, int L3>
-__device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P, int i) {
+__device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P, int i, EdgeLists& L) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
   const int lane = int(threadIdx.x);
   const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
   const bool gy_on = a.want_gy && L2 > 0;
   const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   int q0 = 0;
-  // the row's edges 64 at a time: activity, slot and sender of edge e0 + lane loaded
-  // once, in parallel, then broadcast edge by edge (no dependent load per edge)
-  for (int e0 = rb; e0 < re; e0 += kWave) {
-    const int my_e = e0 + lane;
-    const bool my_act = my_e < re && edge_active(a, my_e);
-    const unsigned long long bal = __ballot(my_act);
-    const int my_s = rb + q0 + __popcll(bal & lt);
-    const int my_j = my_act ? a.act_j[my_s] : 0;
-    q0 += __popcll(bal);
-    const int cnt = min(kWave, re - e0);
-  for (int k = 0; k < cnt; ++k) {
-    const int e = e0 + k;
-    if (!((bal >> k) & 1ull)) {
-      if (a.grad_w)
-        for (int u = lane; u < P.mul; u += kWave) a.grad_w[(long)e * a.w_stride + P.w_off + u] = 0.0f;
-      continue;
+  for (int g0 = rb; g0 < re; g0 += kSeg) {
+    const int g1 = min(re, g0 + kSeg);
+    int nact = 0, nz = 0;
+    for (int c0 = g0; c0 < g1; c0 += kWave) {
+      const int my_e = c0 + lane;
+      const bool in = my_e < g1;
+      const bool act = in && edge_active(a, my_e);
+      const unsigned long long ba = __ballot(act), bz = __ballot(in && !act);
+      if (act) {
+        const int r = nact + __popcll(ba & lt);
+        const int sl = rb + q0 + r;
+        L.e[r] = my_e;
+        L.s[r] = sl;
+        L.j[r] = a.act_j[sl];
+      } else if (in) {
+        L.z[nz + __popcll(bz & lt)] = my_e;
+      }
+      nact += __popcll(ba);
+      nz += __popcll(bz);
     }
-    const int s = __shfl(my_s, k, kWave);
-    const int j = __shfl(my_j, k, kWave);
-    float Y[N2];
+    __syncthreads();
+    if (a.grad_w)
+      for (int k = 0; k < nz; ++k) {
+        const long row = (long)L.z[k] * a.w_stride + P.w_off;
+        for (int u = lane; u < P.mul; u += kWave) a.grad_w[row + u] = 0.0f;
+      }
+    for (int uc = 0; uc < P.mul && nact > 0; uc += kChunks * kWave) {
+      bool ok[kChunks];
+      float go[kChunks][N3];
 #pragma unroll
-    for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
-    float A[N1][N3];
-    form_a<L1, L2, L3>(Y, A);
-    float gy[N2];
+      for (int c = 0; c < kChunks; ++c) {
+        const int u = uc + c * kWave + lane;
+        ok[c] = u < P.mul;
+        const int uu = ok[c] ? u : 0;
 #pragma unroll
-    for (int m = 0; m < N2; ++m) gy[m] = 0.0f;
-    for (int u = lane; u < P.mul; u += kWave) {
-      float xv[N1], go[N3];
+        for (int m = 0; m < N3; ++m) go[c][m] = a.grad_out[(long)i * a.f_out + P.out_off + uu * N3 + m];
+      }
+      struct Edge {
+        float Y[N2];
+        float x[kChunks][N1];
+        float w[kChunks];
+      };
+      auto load = [&](int k, Edge& d) {
+        const int s = L.s[k], e = L.e[k], j = L.j[k];
 #pragma unroll
-      for (int m = 0; m < N1; ++m) xv[m] = a.x[(long)j * a.f_in + P.in_off + u * N1 + m];
+        for (int m = 0; m < N2; ++m) d.Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
 #pragma unroll
-      for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + u * N3 + m];
-      if (a.grad_w) {
-        float gw = 0.0f;
+        for (int c = 0; c < kChunks; ++c) {
+          const int uu = ok[c] ? uc + c * kWave + lane : 0;
 #pragma unroll
-        for (int m3 = 0; m3 < N3; ++m3) {
-          float t = 0.0f;
-#pragma unroll
-          for (int m1 = 0; m1 < N1; ++m1) t = __builtin_fmaf(A[m1][m3], xv[m1], t);
-          gw = __builtin_fmaf(t, go[m3], gw);
+          for (int m = 0; m < N1; ++m) d.x[c][m] = a.x[(long)j * a.f_in + P.in_off + uu * N1 + m];
+          d.w[c] = gy_on ? a.w[(long)e * a.w_stride + P.w_off + uu] : 0.0f;
         }
-        a.grad_w[(long)e * a.w_stride + P.w_off + u] = gw;
-      }
-      if (gy_on) {
-        const float wv = a.w[(long)e * a.w_stride + P.w_off + u];
+      };
+      Edge cur, nxt;
+      load(0, nxt);
+      for (int k = 0; k < nact; ++k) {
+        cur = nxt;
+        load(min(k + 1, nact - 1), nxt);
+        const int s = L.s[k], e = L.e[k];
+        float A[N1][N3];
+        form_a<L1, L2, L3>(cur.Y, A);
+        float gy[N2];
 #pragma unroll
-        for (int m = 0; m < N1; ++m) xv[m] *= wv;
-        sfor<0, N1>([&](auto M1) {
-          sfor<0, N2>([&](auto M2) {
-            sfor<0, N3>([&](auto M3) {
-              constexpr float c =
-                  kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
-              if constexpr (c != 0.0f)
-                gy[decltype(M2)::value] =
-                    __builtin_fmaf(c * xv[decltype(M1)::value], go[decltype(M3)::value], gy[decltype(M2)::value]);
+        for (int m = 0; m < N2; ++m) gy[m] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+          if (!ok[c]) continue;
+          if (a.grad_w) {
+            float gw = 0.0f;
+#pragma unroll
+            for (int m3 = 0; m3 < N3; ++m3) {
+              float t = 0.0f;
+#pragma unroll
+              for (int m1 = 0; m1 < N1; ++m1) t = __builtin_fmaf(A[m1][m3], cur.x[c][m1], t);
+              gw = __builtin_fmaf(t, go[c][m3], gw);
+            }
+            a.grad_w[(long)e * a.w_stride + P.w_off + uc + c * kWave + lane] = gw;
+          }
+          if (gy_on) {
+            float xw[N1];
+#pragma unroll
+            for (int m = 0; m < N1; ++m) xw[m] = cur.x[c][m] * cur.w[c];
+            sfor<0, N1>([&](auto M1) {
+              sfor<0, N2>([&](auto M2) {
+                sfor<0, N3>([&](auto M3) {
+                  constexpr float cg =
+                      kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
+                  if constexpr (cg != 0.0f)
+                    gy[decltype(M2)::value] = __builtin_fmaf(cg * xw[decltype(M1)::value], go[c][decltype(M3)::value],
+                                                             gy[decltype(M2)::value]);
+                });
+              });
             });
-          });
-        });
-      }
-    }
-    if (gy_on) {
+          }
+        }
+        if (gy_on) {
 #pragma unroll
-      for (int m = 0; m < N2; ++m) {
-        const float v = wave_sum(gy[m]);
-        if (lane == 0) a.gyp[(long)s * a.gy_stride + P.gy_off + m] = v;
+          for (int m = 0; m < N2; ++m) {
+            const float v = wave_sum(gy[m]);
+            if (lane == 0) {
+              // channel blocks past the first add to the partial of the first
+              const long at = (long)s * a.gy_stride + P.gy_off + m;
+              a.gyp[at] = uc == 0 ? v : a.gyp[at] + v;
+            }
+          }
+        }
       }
     }
-  }
+    q0 += nact;
+    __syncthreads();   // the lists are read before the next segment overwrites them
   }
 }
 
 __global__ void __launch_bounds__(kWave) bwd_edge_kernel(BwdArgs a) {
+  __shared__ EdgeLists L;
   const int i = int(blockIdx.x);
   const PathDev P = a.paths[blockIdx.y];
   by_variant<0, kNumVariants>(P.variant, [&](auto V) {
     constexpr VariantDesc d = variant_desc(decltype(V)::value);
-    bwd_edge_path<d.l1, d.l2, d.l3>(a, P, i);
+    bwd_edge_path<d.l1, d.l2, d.l3>(a, P, i, L);
   });
 }
 
