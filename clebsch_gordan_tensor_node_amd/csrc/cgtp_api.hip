@@ -781,10 +781,13 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
       per_block += 1 << (G.lanes_log2 - lg_min);
     }
     const int64_t block = 64 >> lg_min;
-    const int64_t wgs = (n_nodes + block - 1) / block * per_block;
+    const int64_t nblocks = (n_nodes + block - 1) / block;
+    // whole rounds of kXcds blocks: blocks past the last are empty workgroups
+    const int64_t wgs = (nblocks + kXcds - 1) / kXcds * kXcds * per_block;
     if (wgs > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
     a.blk_wgs = per_block;
     a.blk_lg_min = lg_min;
+    a.n_blocks = int(nblocks);
     a.total_wgs = int(wgs);
     CGTP_HIP(launch_conv(a, L.cls, s, li == 0 ? ev_begin : nullptr, li + 1 == launches.size() ? ev_end : nullptr));
   }

@@ -49,6 +49,7 @@ struct Group {
 // whose range starts at or before it in g_start (two wide scalar loads, no dependent
 // loads), then reads its group's record with one more.
 constexpr int kMaxGroupsPerLaunch = 32;
+constexpr int kXcds = 8;   // accelerator dies of an MI355X, each with its own L2
 
 struct alignas(32) GroupArgs {
   int32_t start;       // first workgroup of the group inside a block
@@ -79,6 +80,7 @@ struct ConvArgsT {
   int32_t total_wgs;          // workgroups of this launch (whole blocks)
   int32_t blk_wgs;            // workgroups per block of 64 / 2^blk_lg_min receivers
   int32_t blk_lg_min;         // smallest lanes_log2 of the launch's groups
+  int32_t n_blocks;           // receiver blocks (workgroup b of block k runs on XCD k mod kXcds)
   int32_t g_start[kMaxGroupsPerLaunch];       // first workgroup of each group inside a block
                                               // (INT32_MAX past the launch's groups)
   GroupArgs grp[kMaxGroupsPerLaunch];

@@ -478,8 +478,15 @@ __device__ __forceinline__ void dispatch(int v, const ConvArgsT<T>& a, const Job
 // runs the first job's code path, which fixes l1, K and the channel block it gathers.
 template <int C, typename T>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgsT<T> a) {
-  const int blk = int(blockIdx.x) / a.blk_wgs;
-  const int wg = int(blockIdx.x) - blk * a.blk_wgs;
+  // the hardware deals workgroups to the XCDs round-robin by index; the numbering puts
+  // every workgroup of one receiver block on the same XCD, so that the block's groups
+  // share the senders' rows and the edges' harmonics in that XCD's L2
+  const int xcd = int(blockIdx.x) % kXcds;
+  const int rr = int(blockIdx.x) / kXcds;
+  const int rb = rr / a.blk_wgs;
+  const int wg = rr - rb * a.blk_wgs;
+  const int blk = rb * kXcds + xcd;
+  if (blk >= a.n_blocks) return;   // padding of the last round of blocks
   // the workgroup's group: the last g with g_start[g] <= wg (g_start is increasing, and
   // INT32_MAX past the launch's groups); the sign bit of g_start - wg - 1 counts it
   uint32_t g = 0;
