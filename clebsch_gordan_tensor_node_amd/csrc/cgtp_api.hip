@@ -732,9 +732,15 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
-  CGTP_HIP(launch_rows(g, P->l_sh_max, s));
-  // 2. node order by active degree (LunaTP Table 9), as position-indexed node records
-  CGTP_HIP(launch_degree_order(ws.deg, int(n_nodes), row_ptr, ws.node_info, s));
+  // 2. node order by active degree (LunaTP Table 9), as position-indexed node records;
+  //    without mask and gate every edge is active and the order needs only row_ptr, so
+  //    it runs in the same launch as the per-row pass
+  if (!mask && !gate) {
+    CGTP_HIP(launch_rows_order(g, P->l_sh_max, ws.node_info, s));
+  } else {
+    CGTP_HIP(launch_rows(g, P->l_sh_max, s));
+    CGTP_HIP(launch_degree_order(ws.deg, int(n_nodes), row_ptr, ws.node_info, s));
+  }
   // 3. the fused convolution: per kernel class, launches of up to kMaxGroupsPerLaunch
   //    job groups whose workgroup ranges travel in the kernel arguments
   ConvArgsT<T> a{};

@@ -337,15 +337,16 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
 
 constexpr int kOrderBins = kScanThreads;
 
-__global__ void __launch_bounds__(kScanThreads) degree_order_kernel(const int32_t* __restrict__ deg, int n,
-                                                                    const int32_t* __restrict__ row_ptr,
-                                                                    int4* __restrict__ node_info) {
+// deg may be null: then every edge is active and deg[i] = row_ptr[i + 1] - row_ptr[i]
+__device__ inline void degree_order_body(const int32_t* __restrict__ deg, int n, const int32_t* __restrict__ row_ptr,
+                                         int4* __restrict__ node_info) {
   __shared__ int wsum[kScanWaves + 1];
   __shared__ int cursor[kOrderBins];
   const int tid = threadIdx.x;
+  auto degree = [&](int i) { return deg ? deg[i] : row_ptr[i + 1] - row_ptr[i]; };
   cursor[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kScanThreads) atomicAdd(&cursor[min(deg[i], kOrderBins - 1)], 1);
+  for (int i = tid; i < n; i += kScanThreads) atomicAdd(&cursor[min(degree(i), kOrderBins - 1)], 1);
   __syncthreads();
   // exclusive scan over the bins from the top degree down
   const int b = kOrderBins - 1 - tid;
@@ -355,10 +356,16 @@ __global__ void __launch_bounds__(kScanThreads) degree_order_kernel(const int32_
   cursor[b] = ex;
   __syncthreads();
   for (int i = tid; i < n; i += kScanThreads) {
-    const int d = deg[i];
+    const int d = degree(i);
     const int pos = atomicAdd(&cursor[min(d, kOrderBins - 1)], 1);
     node_info[pos] = make_int4(i, row_ptr[i], d, 0);
   }
+}
+
+__global__ void __launch_bounds__(kScanThreads) degree_order_kernel(const int32_t* __restrict__ deg, int n,
+                                                                    const int32_t* __restrict__ row_ptr,
+                                                                    int4* __restrict__ node_info) {
+  degree_order_body(deg, n, row_ptr, node_info);
 }
 
 // ---------------------------------------------------------------------------------
@@ -392,8 +399,7 @@ constexpr int kRowThreads = 256;
 // q-th active edge of row i goes to slot row_ptr[i] + q (q from a ballot prefix).  With
 // no mask the slot is the edge itself.
 template <int L, typename P>
-__global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs<P> a) {
-  const int row = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kRowThreads / kWave) + int(threadIdx.x) / kWave);
+__device__ inline void edge_rows_body(const RowArgs<P>& a, int row) {
   if (row >= a.n_nodes) return;
   const int lane = lane_id();
   const unsigned long long lt_mask = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
@@ -443,6 +449,25 @@ __global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs<P> a) {
     for (int q = NY; q < a.sh_stride; ++q) out[q] = P(0);
   }
   if (a.deg && lane == 0) a.deg[row] = cnt;
+}
+
+template <int L, typename P>
+__global__ void __launch_bounds__(kRowThreads) edge_rows_kernel(RowArgs<P> a) {
+  edge_rows_body<L, P>(a, __builtin_amdgcn_readfirstlane(int(blockIdx.x) * (kRowThreads / kWave) +
+                                                         int(threadIdx.x) / kWave));
+}
+
+// The per-row pass and the node order in one launch, for a forward without mask and gate
+// (every edge active, so the degrees are the row lengths): workgroup 0 builds the node
+// records from row_ptr while the others run the per-row pass, one wave per row.
+template <int L, typename P>
+__global__ void __launch_bounds__(kScanThreads) rows_order_kernel(RowArgs<P> a, int4* node_info) {
+  if (blockIdx.x == 0) {
+    degree_order_body(nullptr, a.n_nodes, a.row_ptr, node_info);
+    return;
+  }
+  edge_rows_body<L, P>(a, __builtin_amdgcn_readfirstlane(int(blockIdx.x - 1) * kScanWaves +
+                                                         int(threadIdx.x) / kWave));
 }
 
 // ---------------------------------------------------------------------------------
@@ -604,6 +629,40 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
     case 4: edge_rows_kernel<4, float><<<nb, kRowThreads, 0, s>>>(a); break;
     case 5: edge_rows_kernel<5, float><<<nb, kRowThreads, 0, s>>>(a); break;
     case 6: edge_rows_kernel<6, float><<<nb, kRowThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_order(const RowPass& p, int l_sh_max, int4* node_info, hipStream_t s) {
+  if (p.n_nodes == 0) return hipSuccess;
+  if (!p.row_ptr || p.mask || p.gate || p.gate64 || !node_info) return hipErrorInvalidValue;
+  const bool f64 = p.pos64 || p.sh64;
+  if (f64 && (p.pos || p.sh)) return hipErrorInvalidValue;
+  const bool has_sh = p.sh || p.sh64;
+  if ((has_sh || p.act_j) && p.n_edges > 0 && !p.col) return hipErrorInvalidValue;
+  if (has_sh && p.n_edges > 0 && !(p.pos || p.pos64)) return hipErrorInvalidValue;
+  const int nb = 1 + ceil_div(p.n_nodes, kScanWaves);
+  if (f64) {
+    const RowArgs<double> a = row_args<double>(p, p.pos64, nullptr, p.sh64, l_sh_max);
+    switch (l_sh_max) {
+      case 0: rows_order_kernel<0, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+      case 1: rows_order_kernel<1, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+      case 2: rows_order_kernel<2, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+      case 3: rows_order_kernel<3, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const RowArgs<float> a = row_args<float>(p, p.pos, nullptr, p.sh, l_sh_max);
+  switch (l_sh_max) {
+    case 0: rows_order_kernel<0, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 1: rows_order_kernel<1, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 2: rows_order_kernel<2, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 3: rows_order_kernel<3, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 4: rows_order_kernel<4, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 5: rows_order_kernel<5, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+    case 6: rows_order_kernel<6, float><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

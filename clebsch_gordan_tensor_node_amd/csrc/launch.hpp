@@ -62,6 +62,9 @@ struct RowPass {
   double cell[9];
 };
 hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s);
+// launch_rows and launch_degree_order in one launch, for a pass without mask and gate
+// (the degrees are the row lengths); deg is still written when requested.
+hipError_t launch_rows_order(const RowPass& p, int l_sh_max, int4* node_info, hipStream_t s);
 
 // One workgroup: optional exclusive scan of deg into act_row_ptr and the node order by
 // deg descending, ties by id ascending, into order (may be null).
