@@ -269,8 +269,8 @@ __global__ void __launch_bounds__(256) bwd_t_count_kernel(BwdArgs a, int32_t* cn
   }
 }
 
-// one workgroup: out[k] = sum_{q < k} in[q], k <= n
-__global__ void __launch_bounds__(1024) bwd_scan_kernel(const int32_t* in, int32_t* out, int n) {
+// one workgroup: out[k] = sum_{q < k} in[q], k <= n; in is reset to zero
+__global__ void __launch_bounds__(1024) bwd_scan_kernel(int32_t* in, int32_t* out, int n) {
   __shared__ int wsum[1024 / kWave + 1];
   const int lane = int(threadIdx.x) & (kWave - 1), wave = int(threadIdx.x) / kWave;
   int carry = 0;
@@ -295,7 +295,10 @@ __global__ void __launch_bounds__(1024) bwd_scan_kernel(const int32_t* in, int32
       wsum[1024 / kWave] = run;
     }
     __syncthreads();
-    if (idx < n) out[idx] = carry + wsum[wave] + inc - v;
+    if (idx < n) {
+      out[idx] = carry + wsum[wave] + inc - v;
+      in[idx] = 0;   // the counts become the placement cursors
+    }
     carry += wsum[1024 / kWave];
     __syncthreads();
   }
@@ -352,24 +355,36 @@ template <int L1, int L2, int L3>
 __device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int cnt, int my_s, int my_i,
                                            int my_e, int u, bool ok, float* acc) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  for (int k = 0; k < cnt; ++k) {
-    const int s = __shfl(my_s, k, kWave), i = __shfl(my_i, k, kWave), e = __shfl(my_e, k, kWave);
+  // one-deep pipeline: entry k + 1's harmonics, weight and grad_out rows are loaded
+  // (at a clamped index, unconditionally) while entry k is used
+  struct Entry {
     float Y[N2];
+    float w;
+    float go[N3];
+  };
+  const int uu = ok ? u : 0;
+  auto load = [&](int k, Entry& d) {
+    const int s = __shfl(my_s, k, kWave), i = __shfl(my_i, k, kWave), e = __shfl(my_e, k, kWave);
 #pragma unroll
-    for (int m = 0; m < N2; ++m) Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
+    for (int m = 0; m < N2; ++m) d.Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
+    d.w = a.w[(long)e * a.w_stride + P.w_off + uu];
+#pragma unroll
+    for (int m = 0; m < N3; ++m) d.go[m] = a.grad_out[(long)i * a.f_out + P.out_off + uu * N3 + m];
+  };
+  Entry cur, nxt;
+  load(0, nxt);
+  for (int k = 0; k < cnt; ++k) {
+    cur = nxt;
+    load(min(k + 1, cnt - 1), nxt);
     float A[N1][N3];
-    form_a<L1, L2, L3>(Y, A);
+    form_a<L1, L2, L3>(cur.Y, A);
     if (ok) {
-      const float wv = a.w[(long)e * a.w_stride + P.w_off + u];
-      float go[N3];
-#pragma unroll
-      for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + u * N3 + m];
 #pragma unroll
       for (int m1 = 0; m1 < N1; ++m1) {
         float t = 0.0f;
 #pragma unroll
-        for (int m3 = 0; m3 < N3; ++m3) t = __builtin_fmaf(A[m1][m3], go[m3], t);
-        acc[m1] = __builtin_fmaf(wv, t, acc[m1]);
+        for (int m3 = 0; m3 < N3; ++m3) t = __builtin_fmaf(A[m1][m3], cur.go[m3], t);
+        acc[m1] = __builtin_fmaf(cur.w, t, acc[m1]);
       }
     }
   }
@@ -494,22 +509,33 @@ __global__ void __launch_bounds__(256) bwd_force_kernel(BwdArgs a) {
   }
 }
 
-// one thread per node: + its edges as sender, - its edges as receiver, in slot order
-__global__ void bwd_pos_kernel(BwdArgs a) {
-  const int n = int(blockIdx.x * blockDim.x + threadIdx.x);
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+// one wave per node: + its edges as sender, - its edges as receiver; lanes take the
+// entries in slot order and a fixed butterfly sums them (fp64)
+__global__ void __launch_bounds__(256) bwd_pos_kernel(BwdArgs a) {
+  const int n = int(blockIdx.x) * (256 / kWave) + int(threadIdx.x) / kWave;
   if (n >= a.n_nodes) return;
+  const int lane = int(threadIdx.x) & (kWave - 1);
   double g[3] = {0.0, 0.0, 0.0};
-  for (int k = a.t_row_ptr[n]; k < a.t_row_ptr[n + 1]; ++k) {
+  for (int k = a.t_row_ptr[n] + lane; k < a.t_row_ptr[n + 1]; k += kWave) {
     const int s = a.t_slot[k];
 #pragma unroll
     for (int c = 0; c < 3; ++c) g[c] += double(a.grad_r[(long)s * 3 + c]);
   }
   const int rb = a.row_ptr[n], d = a.deg[n];
-  for (int q = 0; q < d; ++q)
+  for (int q = lane; q < d; q += kWave)
 #pragma unroll
     for (int c = 0; c < 3; ++c) g[c] -= double(a.grad_r[(long)(rb + q) * 3 + c]);
 #pragma unroll
-  for (int c = 0; c < 3; ++c) a.grad_pos[3 * n + c] = float(g[c]);
+  for (int c = 0; c < 3; ++c) {
+    const double v = wave_sum_f64(g[c]);
+    if (lane == 0) a.grad_pos[3 * n + c] = float(v);
+  }
 }
 
 }  // namespace
@@ -528,7 +554,6 @@ hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row
   fill_zero_kernel<<<zb, 256, 0, s>>>(t_cnt, n);
   bwd_t_count_kernel<<<rb, 256, 0, s>>>(a, t_cnt, nullptr, nullptr, 0);
   bwd_scan_kernel<<<1, 1024, 0, s>>>(t_cnt, t_row_ptr, n);
-  fill_zero_kernel<<<zb, 256, 0, s>>>(t_cnt, n);
   BwdArgs b = a;
   b.t_row_ptr = t_row_ptr;
   bwd_t_count_kernel<<<rb, 256, 0, s>>>(b, t_cnt, t_slot, t_recv, 1);
@@ -546,7 +571,7 @@ hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s) {
   const int n = a.n_nodes;
   if (n == 0) return hipSuccess;
   bwd_force_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
-  bwd_pos_kernel<<<ceil_div(n, 256), 256, 0, s>>>(a);
+  bwd_pos_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
