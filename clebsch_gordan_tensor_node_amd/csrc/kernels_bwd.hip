@@ -98,20 +98,17 @@ __device__ __forceinline__ void form_a(const float* Y, float (*A)[2 * L3 + 1]) {
 // ---------------------------------------------------------------------------------
 
 constexpr int kSeg = 256;      // active edges of a row listed in LDS at a time
-constexpr int kChunks = 2;     // channel chunks of 64 lanes held in registers (128 channels)
+constexpr int kChunks = 2;     // channel chunks of 64 lanes in the direct form (128 channels)
 
 struct EdgeLists {
   int e[kSeg], s[kSeg], j[kSeg], z[kSeg];   // active: edge, slot, sender; inactive: edge
 };
 
-// One wave per (receiver i, path).  Per segment of the row: the active edges (edge id,
-// slot, sender) are compacted into LDS and the w-gradient rows of the inactive ones are
-// zeroed with coalesced stores; then the active edges are walked with a one-deep
-// pipeline: the next edge's harmonics, x_j and weights are loaded (unconditionally, at a
-// clamped index) while the current edge is computed.  Channels u = uc + 64 c + lane,
-// c < kChunks, with grad_out of the row held in registers.
+// The direct form: A = C.Y per edge, then the w-gradient and dL/dY per channel, two
+// 64-channel chunks per walk of the row's edges (for couplings whose folded form, below,
+// is too large to hold twice in registers).
 template <int L1, int L2, int L3>
-__device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P, int i, EdgeLists& L) {
+__device__ __forceinline__ void bwd_edge_path_direct(const BwdArgs& a, const PathDev& P, int i, EdgeLists& L) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
   const int lane = int(threadIdx.x);
   const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
@@ -232,13 +229,156 @@ __device__ __forceinline__ void bwd_edge_path(const BwdArgs& a, const PathDev& P
   }
 }
 
+// One wave per (receiver i, path).  Per segment of the row: the active edges (edge id,
+// slot, sender) are compacted into LDS and the w-gradient rows of the inactive ones are
+// zeroed with coalesced stores; then the active edges are walked with a one-deep
+// pipeline: the next edge's harmonics, x_j and weights are loaded (unconditionally, at a
+// clamped index) while the current edge is computed.  Channels u = uc + 64 c + lane,
+// c < NC (1 for paths of at most 64 channels, else 2), with the row's grad_out folded
+// into the coupling once (B below).
+template <int L1, int L2, int L3, int NC>
+__device__ __forceinline__ void bwd_edge_path_folded(const BwdArgs& a, const PathDev& P, int i, EdgeLists& L) {
+  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
+  const int lane = int(threadIdx.x);
+  const int rb = a.row_ptr[i], re = a.row_ptr[i + 1];
+  const bool gy_on = a.want_gy && L2 > 0;
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int q0 = 0;
+  for (int g0 = rb; g0 < re; g0 += kSeg) {
+    const int g1 = min(re, g0 + kSeg);
+    int nact = 0, nz = 0;
+    for (int c0 = g0; c0 < g1; c0 += kWave) {
+      const int my_e = c0 + lane;
+      const bool in = my_e < g1;
+      const bool act = in && edge_active(a, my_e);
+      const unsigned long long ba = __ballot(act), bz = __ballot(in && !act);
+      if (act) {
+        const int r = nact + __popcll(ba & lt);
+        const int sl = rb + q0 + r;
+        L.e[r] = my_e;
+        L.s[r] = sl;
+        L.j[r] = a.act_j[sl];
+      } else if (in) {
+        L.z[nz + __popcll(bz & lt)] = my_e;
+      }
+      nact += __popcll(ba);
+      nz += __popcll(bz);
+    }
+    __syncthreads();
+    if (a.grad_w)
+      for (int k = 0; k < nz; ++k) {
+        const long row = (long)L.z[k] * a.w_stride + P.w_off;
+        for (int u = lane; u < P.mul; u += kWave) a.grad_w[row + u] = 0.0f;
+      }
+    for (int uc = 0; uc < P.mul && nact > 0; uc += NC * kWave) {
+      bool ok[NC];
+      int uu[NC];
+      // B[c][m1][m2] = sum_m3 C[m1,m2,m3] g[m3]: the receiver's output gradient folded
+      // into the coupling once per row and channel; per edge then
+      //   dL/dw = sum_m1 x[m1] sum_m2 B[m1][m2] Y[m2],  dL/dY[m2] += w sum_m1 x[m1] B[m1][m2]
+      float B[NC][N1][N2];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const int u = uc + c * kWave + lane;
+        ok[c] = u < P.mul;
+        uu[c] = ok[c] ? u : 0;
+        float go[N3];
+#pragma unroll
+        for (int m = 0; m < N3; ++m) go[m] = a.grad_out[(long)i * a.f_out + P.out_off + uu[c] * N3 + m];
+        sfor<0, N1>([&](auto M1) {
+          sfor<0, N2>([&](auto M2) {
+            float b = 0.0f;
+            sfor<0, N3>([&](auto M3) {
+              constexpr float cg =
+                  kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
+              if constexpr (cg != 0.0f) b = __builtin_fmaf(cg, go[decltype(M3)::value], b);
+            });
+            B[c][decltype(M1)::value][decltype(M2)::value] = b;
+          });
+        });
+      }
+      struct Edge {
+        float Y[N2];
+        float x[NC][N1];
+        float w[NC];
+      };
+      auto load = [&](int k, Edge& d) {
+        const int s = L.s[k], e = L.e[k], j = L.j[k];
+#pragma unroll
+        for (int m = 0; m < N2; ++m) d.Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+          for (int m = 0; m < N1; ++m) d.x[c][m] = a.x[(long)j * a.f_in + P.in_off + uu[c] * N1 + m];
+          d.w[c] = gy_on ? a.w[(long)e * a.w_stride + P.w_off + uu[c]] : 0.0f;
+        }
+      };
+      Edge cur, nxt;
+      load(0, nxt);
+      for (int k = 0; k < nact; ++k) {
+        cur = nxt;
+        load(min(k + 1, nact - 1), nxt);
+        const int s = L.s[k], e = L.e[k];
+        float gy[N2];
+#pragma unroll
+        for (int m = 0; m < N2; ++m) gy[m] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if (!ok[c]) continue;
+          if (a.grad_w) {
+            float gw = 0.0f;
+#pragma unroll
+            for (int m1 = 0; m1 < N1; ++m1) {
+              float d = 0.0f;
+#pragma unroll
+              for (int m2 = 0; m2 < N2; ++m2) d = __builtin_fmaf(B[c][m1][m2], cur.Y[m2], d);
+              gw = __builtin_fmaf(cur.x[c][m1], d, gw);
+            }
+            a.grad_w[(long)e * a.w_stride + P.w_off + uc + c * kWave + lane] = gw;
+          }
+          if (gy_on) {
+#pragma unroll
+            for (int m1 = 0; m1 < N1; ++m1) {
+              const float xw = cur.x[c][m1] * cur.w[c];
+#pragma unroll
+              for (int m2 = 0; m2 < N2; ++m2) gy[m2] = __builtin_fmaf(xw, B[c][m1][m2], gy[m2]);
+            }
+          }
+        }
+        if (gy_on) {
+#pragma unroll
+          for (int m = 0; m < N2; ++m) {
+            const float v = wave_sum(gy[m]);
+            if (lane == 0) {
+              // channel blocks past the first add to the partial of the first
+              const long at = (long)s * a.gy_stride + P.gy_off + m;
+              a.gyp[at] = uc == 0 ? v : a.gyp[at] + v;
+            }
+          }
+        }
+      }
+    }
+    q0 += nact;
+    __syncthreads();   // the lists are read before the next segment overwrites them
+  }
+}
+
 __global__ void __launch_bounds__(kWave) bwd_edge_kernel(BwdArgs a) {
   __shared__ EdgeLists L;
   const int i = int(blockIdx.x);
   const PathDev P = a.paths[blockIdx.y];
   by_variant<0, kNumVariants>(P.variant, [&](auto V) {
     constexpr VariantDesc d = variant_desc(decltype(V)::value);
-    bwd_edge_path<d.l1, d.l2, d.l3>(a, P, i, L);
+    // the folded form with one or two 64-channel chunks per walk of the row's edges;
+    // paths of more than 64 channels whose folded coupling is too large to hold twice
+    // take the direct form
+    constexpr bool two = (2 * d.l1 + 1) * (2 * d.l2 + 1) <= 25;
+    if (P.mul <= kWave)
+      bwd_edge_path_folded<d.l1, d.l2, d.l3, 1>(a, P, i, L);
+    else if constexpr (two)
+      bwd_edge_path_folded<d.l1, d.l2, d.l3, 2>(a, P, i, L);
+    else
+      bwd_edge_path_direct<d.l1, d.l2, d.l3>(a, P, i, L);
   });
 }
 
