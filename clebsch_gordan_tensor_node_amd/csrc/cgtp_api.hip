@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -136,6 +137,10 @@ int ilog2(int v) {
 
 using namespace cgtp;
 
+// streams a plan may add beside the caller's: with it, four, the hardware queues a
+// process gets by default
+constexpr int kAuxStreams = 3;
+
 struct cgtp_plan_s {
   std::vector<Irrep> in, sh, out;
   std::vector<PathInfo> paths;
@@ -161,6 +166,26 @@ struct cgtp_plan_s {
   int lmax = 0;                      // largest l of the plan
   PathDev* d_paths = nullptr;
   int32_t* d_irrep = nullptr;
+  // Forward launches: a kernel class and a range of its groups each.  Launches write
+  // disjoint output columns and only read the inputs, so the plan spreads them over the
+  // caller's stream (stream 0) and up to kAuxStreams streams of its own (stream k = aux
+  // stream k - 1), forked from and joined back into the caller's stream by events; the
+  // small latency-bound launches of the l >= 4 classes then run beside the large one.
+  struct ConvLaunch {
+    int cls, g0, g1, stream;
+  };
+  // per group: its heaviest job's cost (per-step work of a lane), its work (cost times
+  // lanes, summed over its jobs) and its weight columns
+  struct GroupLoad {
+    double max_cost, work, cols;
+  };
+  std::vector<GroupLoad> group_load;
+  std::vector<ConvLaunch> launches;  // in enqueue order
+  int n_aux = 0;
+  hipStream_t aux[kAuxStreams] = {};
+  hipEvent_t fork = nullptr;
+  hipEvent_t join[kAuxStreams] = {};
+  std::mutex enqueue;                // held while a forward forks, launches and joins
 };
 
 namespace {
@@ -261,6 +286,7 @@ void schedule(cgtp_plan_s& P) {
     return x.cost > y.cost;
   });
   P.groups.clear();
+  P.group_load.clear();
   P.class_begin.assign(kNumClasses + 1, 0);
   for (const G& g : gs) {
     Group G{};
@@ -280,11 +306,55 @@ void schedule(cgtp_plan_s& P) {
     G.lanes_log2 = std::max(G.lanes_log2, ilog2(next_pow2(G.y4)));
     for (int k = G.first_job; k < G.first_job + G.n_jobs; ++k) P.jobs[k].lanes_log2 = G.lanes_log2;
     P.groups.push_back(G);
+    double work = 0.0, cols = 0.0;
+    for (int k = g.begin; k < g.begin + g.n; ++k) {
+      work += tmp[k].cost * tmp[k].j.n_ch / (64.0 * variant_desc(tmp[k].j.variant).k);
+      cols += tmp[k].j.n_ch;
+    }
+    P.group_load.push_back({g.cost, work, cols});
     P.class_begin[g.cls + 1]++;
   }
   for (int c = 0; c < kNumClasses; ++c) P.class_begin[c + 1] += P.class_begin[c];
   P.n_variants = 0;
   for (int u : used) P.n_variants += u;
+
+  // launches of up to kMaxGroupsPerLaunch groups of one class, spread over the streams
+  // longest first onto the least loaded (the first, the longest, stays on the caller's
+  // stream).  A launch's time is modelled as the largest of three bounds, in
+  // microseconds for a graph of about 20 000 edges (only their ratios matter): the
+  // receiver with the most edges walks them in sequence at a step time set by the
+  // heaviest group, the arithmetic of all groups, and the weight stream.
+  P.launches.clear();
+  for (int c = 0; c < kNumClasses; ++c)
+    for (int g0 = P.class_begin[c]; g0 < P.class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
+      P.launches.push_back({c, g0, std::min(P.class_begin[c + 1], g0 + kMaxGroupsPerLaunch), 0});
+  std::vector<double> est(P.launches.size(), 0.0);
+  for (size_t li = 0; li < P.launches.size(); ++li) {
+    double chain = 0.0, work = 0.0, cols = 0.0;
+    for (int k = P.launches[li].g0; k < P.launches[li].g1; ++k) {
+      chain = std::max(chain, P.group_load[k].max_cost);
+      work += P.group_load[k].work;
+      cols += P.group_load[k].cols;
+    }
+    est[li] = std::max(10.0 + 0.075 * chain, std::max(0.072 * work, 0.026 * cols));
+  }
+  std::vector<int> ord(P.launches.size());
+  for (size_t li = 0; li < ord.size(); ++li) ord[li] = int(li);
+  std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return est[x] > est[y]; });
+  double load[kAuxStreams + 1] = {};
+  std::vector<cgtp_plan_s::ConvLaunch> sorted;
+  P.n_aux = 0;
+  for (int li : ord) {
+    int best = 0;
+    for (int k = 1; k <= kAuxStreams; ++k)
+      if (load[k] < load[best]) best = k;
+    load[best] += est[li];
+    cgtp_plan_s::ConvLaunch L = P.launches[li];
+    L.stream = best;
+    P.n_aux = std::max(P.n_aux, best);
+    sorted.push_back(L);
+  }
+  P.launches = sorted;
 }
 
 
@@ -331,6 +401,17 @@ int check_device(const cgtp_plan_s* P) {
 }
 
 const int kMaxInt32 = 0x7fffffff;
+
+// frees a device plan's tables, streams and events (its device is current)
+void release_device(cgtp_plan_s* P) {
+  if (P->d_tables) (void)hipFree(P->d_tables);
+  for (int k = 0; k < kAuxStreams; ++k) {
+    if (P->aux[k]) (void)hipStreamDestroy(P->aux[k]);
+    if (P->join[k]) (void)hipEventDestroy(P->join[k]);
+  }
+  if (P->fork) (void)hipEventDestroy(P->fork);
+  P->d_tables = nullptr;
+}
 
 }  // namespace
 
@@ -508,10 +589,17 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
         e = hipMemcpy(P->d_paths, P->pdev.data(), P->pdev.size() * sizeof(PathDev), hipMemcpyHostToDevice);
       if (e == hipSuccess) e = hipMemcpy(P->d_irrep, P->irrep_tab.data(), ib, hipMemcpyHostToDevice);
     }
+    // auxiliary streams (default priority, not synchronising with the null stream) and
+    // the fork/join events of the concurrent launches
+    for (int k = 0; e == hipSuccess && k < P->n_aux; ++k) {
+      e = hipStreamCreateWithFlags(&P->aux[k], hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&P->join[k], hipEventDisableTiming);
+    }
+    if (e == hipSuccess && P->n_aux > 0) e = hipEventCreateWithFlags(&P->fork, hipEventDisableTiming);
     if (e != hipSuccess) {
-      if (P->d_tables) (void)hipFree(P->d_tables);
+      release_device(P);
       delete P;
-      return fail(CGTP_ERR_HIP, "job table upload: %s", hipGetErrorString(e));
+      return fail(CGTP_ERR_HIP, "plan device set-up: %s", hipGetErrorString(e));
     }
   }
   *out = P;
@@ -520,11 +608,11 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
 
 void cgtp_plan_destroy(cgtp_plan_t plan) {
   if (!plan) return;
-  if (plan->d_tables) {
+  if (!plan->host_only) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != plan->device) (void)hipSetDevice(plan->device);
-    (void)hipFree(plan->d_tables);
+    release_device(plan);
     if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
   }
   delete plan;
@@ -757,18 +845,10 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
   a.sh_stride = P->sh_pad;
-  struct Launch {
-    int cls, g0, g1;
-  };
-  std::vector<Launch> launches;
-  for (int c = 0; c < kNumClasses; ++c)
-    for (int g0 = P->class_begin[c]; g0 < P->class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
-      launches.push_back(Launch{c, g0, std::min(P->class_begin[c + 1], g0 + kMaxGroupsPerLaunch)});
   // Workgroups are dispatched block by block: a block of B = 64 / 2^lg_min receivers
   // (the largest node group of the launch) holds B / S_g node groups of every group g, so
   // the groups of one block, which read the same weight rows, run at the same time.
-  for (size_t li = 0; li < launches.size(); ++li) {
-    const Launch& L = launches[li];
+  auto fill = [&](const cgtp_plan_s::ConvLaunch& L) -> int64_t {
     a.n_groups = L.g1 - L.g0;
     for (int k = 0; k < kMaxGroupsPerLaunch; ++k) a.g_start[k] = kMaxInt32;   // past the groups
     int lg_min = 6;
@@ -790,15 +870,41 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
     const int64_t nblocks = (n_nodes + block - 1) / block;
     // whole rounds of kXcds blocks: blocks past the last are empty workgroups
     const int64_t wgs = (nblocks + kXcds - 1) / kXcds * kXcds * per_block;
-    if (wgs > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
     a.blk_wgs = per_block;
     a.blk_lg_min = lg_min;
     a.n_blocks = int(nblocks);
-    a.total_wgs = int(wgs);
-    CGTP_HIP(launch_conv(a, L.cls, s, li == 0 ? ev_begin : nullptr, li + 1 == launches.size() ? ev_end : nullptr));
+    a.total_wgs = int(std::min<int64_t>(wgs, kMaxInt32));
+    return wgs;
+  };
+  const auto& launches = P->launches;
+  for (const auto& L : launches)
+    if (fill(L) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
+  // With auxiliary streams: fork them from the caller's stream after the per-row pass,
+  // launch, and join them back; the events then bracket the whole set (enqueue-time
+  // records).  On one stream the events are stamped by the first and last launches.
+  const bool forked = P->n_aux > 0;
+  std::unique_lock<std::mutex> lock(P->enqueue, std::defer_lock);
+  if (forked) {
+    lock.lock();
+    if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
+    CGTP_HIP(hipEventRecord(P->fork, s));
+    for (int k = 0; k < P->n_aux; ++k) CGTP_HIP(hipStreamWaitEvent(P->aux[k], P->fork, 0));
   }
-  const int first_cls = launches.empty() ? -1 : launches.front().cls;
-  if (first_cls < 0) {  // no wave task (cannot happen with n_nodes > 0): keep the events valid
+  for (size_t li = 0; li < launches.size(); ++li) {
+    const auto& L = launches[li];
+    fill(L);
+    hipStream_t ls = L.stream == 0 ? s : P->aux[L.stream - 1];
+    CGTP_HIP(launch_conv(a, L.cls, ls, !forked && li == 0 ? ev_begin : nullptr,
+                         !forked && li + 1 == launches.size() ? ev_end : nullptr));
+  }
+  if (forked) {
+    for (int k = 0; k < P->n_aux; ++k) {
+      CGTP_HIP(hipEventRecord(P->join[k], P->aux[k]));
+      CGTP_HIP(hipStreamWaitEvent(s, P->join[k], 0));
+    }
+    if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));
+  }
+  if (launches.empty()) {  // no wave task (cannot happen with n_nodes > 0): keep the events valid
     if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
     if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));
   }

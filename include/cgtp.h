@@ -38,8 +38,11 @@
  * Ownership: the caller allocates and owns every device buffer, including the
  * workspace; the library never allocates in cgtp_neighbors_build, cgtp_conv_prepare,
  * cgtp_conv_forward or cgtp_edge_sh and keeps no pointer after a call returns.  A plan
- * owns only its small device tables (freed by cgtp_plan_destroy); a plan is immutable
- * after creation and may be shared by threads and streams.
+ * owns its small device tables and, when its forward takes several kernel launches (plans
+ * with paths of l >= 4, or more path groups than one launch carries), up to three HIP
+ * streams and four events of its own (all freed by cgtp_plan_destroy).  A plan's tables
+ * are immutable after creation; it may be shared by threads and streams (forward calls
+ * on one plan take a per-plan lock while they enqueue).
  * Asynchrony: device work is enqueued on `stream` (a hipStream_t; NULL = default
  * stream) and not waited for, except where stated.  Inputs must stay valid until the
  * stream reaches that point.
@@ -151,7 +154,11 @@ int cgtp_edge_sh(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const floa
  * Arguments as above; x [n_nodes, f_in], w [n_edges, w_per_edge], mask NULL = all
  * active.  All device pointers 16-byte aligned; x must be smaller than 4 GiB (the
  * kernel addresses it with 32-bit byte offsets), else CGTP_ERR_UNSUPPORTED.
- * Asynchronous on `stream`.  The result is bitwise reproducible from run to run. */
+ * Asynchronous on `stream`.  The result is bitwise reproducible from run to run.
+ * Launches of different kernel classes write disjoint output columns; when there are
+ * several, the call forks the plan's own streams from `stream` after the per-row pass
+ * and joins them back into `stream` (events), so work enqueued on `stream` after the
+ * call sees the whole output, and the call may be captured into a HIP graph. */
 int cgtp_conv_forward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
                       const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
                       int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
@@ -175,7 +182,9 @@ int cgtp_conv_forward_gated(cgtp_plan_t plan, const float* pos, int64_t n_nodes,
  * (hipEvent_t) ev_conv_begin / ev_conv_end stamped by the dispatch of the fused
  * convolution kernel itself (at the start of its first launch and the end of its last),
  * so that the caller can time that kernel apart from the prepare and harmonics passes
- * and from launch gaps.  Same kernels, same results. */
+ * and from launch gaps.  When the launches are spread over the plan's streams the two
+ * events are recorded on `stream` just before the fork and just after the join instead.
+ * Same kernels, same results. */
 int cgtp_conv_forward_timed(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
                             const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
                             int64_t n_edges, const float* x, const float* w, const uint8_t* mask,

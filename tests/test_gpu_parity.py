@@ -192,6 +192,36 @@ def test_conv_sampled_large(dev, name):
     _compare(got[rows], ref, f"{name}[48 rows]")
 
 
+def test_conv_concurrent_classes_shared_plan(dev):
+    # c5_768 runs six kernel classes (l <= 3, and l >= 4 by l1): their launches go to the
+    # caller's stream and to streams of the plan's own, joined back into the caller's.
+    # One plan shared by two host threads, each on its own torch stream, gives bitwise
+    # the output of a lone call on every call.
+    import threading
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("c5_768")
+    p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    pos_d, rp_d, col_d, sh_d, x_d, w_d = (_t(a, dev) for a in (pos, rp, col, sh, x, w))
+    ref = C.conv_forward(p, pos_d, cell, rp_d, col_d, sh_d, x_d, w_d)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+
+    def work(k):
+        with torch.cuda.stream(streams[k]):
+            for _ in range(4):
+                outs[k].append(C.conv_forward(p, pos_d, cell, rp_d, col_d, sh_d, x_d, w_d))
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert [len(o) for o in outs] == [4, 4]
+    for o in outs[0] + outs[1]:
+        assert torch.equal(o, ref)
+
+
 def _small_system(n, box_len, cutoff, seed):
     rng = np.random.default_rng(seed)
     pos = (rng.random((n, 3)) * box_len).astype(np.float32)
