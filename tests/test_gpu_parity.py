@@ -222,6 +222,34 @@ def test_conv_concurrent_classes_shared_plan(dev):
         assert torch.equal(o, ref)
 
 
+def test_conv_graph_capture_multi_launch(dev):
+    # The forward of a plan with several kernel launches (fork to the plan's streams and
+    # join) captured into a HIP graph: every replay, with eager work and synchronisation
+    # between replays, equals the eager call bit for bit.
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask = _workload("c5_768")
+    p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    pos_d, rp_d, col_d, sh_d, x_d, w_d = (_t(a, dev) for a in (pos, rp, col, sh, x, w))
+    n, e = len(pos), len(col)
+    out = torch.empty((n, p.f_out), dtype=torch.float32, device=dev)
+    ws = torch.empty(p.workspace_size(n, e), dtype=torch.uint8, device=dev)
+    ref = C.conv_forward(p, pos_d, cell, rp_d, col_d, sh_d, x_d, w_d).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        C.conv_forward(p, pos_d, cell, rp_d, col_d, sh_d, x_d, w_d, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), k
+        # eager work between replays: an eager call into another buffer
+        other = C.conv_forward(p, pos_d, cell, rp_d, col_d, sh_d, x_d, w_d)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref), k
+
+
 def _small_system(n, box_len, cutoff, seed):
     rng = np.random.default_rng(seed)
     pos = (rng.random((n, 3)) * box_len).astype(np.float32)
