@@ -266,7 +266,7 @@ def conv_forward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, mask=None, ou
 
 def conv_backward(plan: Plan, pos, cell, row_ptr, col, shift, x, w, grad_out, mask=None, gate=None,
                   need=("x", "w", "pos"), workspace=None):
-    """Gradients of a scalar L with dL/d out = grad_out [N, f_out] (fp32, l <= 3 plans):
+    """Gradients of a scalar L with dL/d out = grad_out [N, f_out] (fp32, l <= 4 plans):
     returns (grad_x [N, f_in], grad_w [E, W], grad_pos [N, 3]); an entry not in `need`
     is None.  Asynchronous on the current stream."""
     lib = load()

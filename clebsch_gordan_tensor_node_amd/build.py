@@ -3,7 +3,8 @@
     python -m clebsch_gordan_tensor_node_amd.build [--incremental] [-j N]
 
 Every translation unit is compiled in parallel; the convolution kernel source is
-compiled once per kernel class (-DCGTP_CONV_CLASS=k).  Objects go to ``_build/`` at the
+compiled once per kernel class (-DCGTP_CONV_CLASS=k), the backward's twice (its edge
+pass and its other passes, -DCGTP_BWD_PART=0/1).  Objects go to ``_build/`` at the
 repository root; the shared library is written next to this file.
 """
 from __future__ import annotations
@@ -40,8 +41,9 @@ def _hipcc() -> str:
 
 
 def _units():
-    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o"),
-             ("kernels_bwd.hip", [], "kernels_bwd.o")]
+    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o")]
+    for part in range(2):   # the backward's edge pass, and its other passes
+        units.append(("kernels_bwd.hip", [f"-DCGTP_BWD_PART={part}"], f"kernels_bwd_p{part}.o"))
     for c in range(N_CONV_CLASSES):
         units.append(("kernels_conv.hip", [f"-DCGTP_CONV_CLASS={c}"], f"kernels_conv_c{c}.o"))
     return units

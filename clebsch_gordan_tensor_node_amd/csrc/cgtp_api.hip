@@ -985,7 +985,9 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
   if (rc != CGTP_OK) return rc;
   if (P->elem != 4) return fail(CGTP_ERR_INVALID_ARG, "the backward is fp32: the plan's precision is fp64");
-  if (P->lmax > 3) return fail(CGTP_ERR_UNSUPPORTED, "the backward supports plans with l <= 3 (this one reaches %d)", P->lmax);
+  if (P->lmax > kBwdLmax)
+    return fail(CGTP_ERR_UNSUPPORTED, "the backward supports plans with l <= %d (this one reaches %d)", kBwdLmax,
+                P->lmax);
   const bool any = grad_x || grad_w || grad_pos;
   if (n_nodes > 0 && any && (!grad_out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
   if (n_edges > 0 && any && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
@@ -1056,10 +1058,10 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   a.has_cell = cell != nullptr;
   for (int k = 0; k < 9; ++k) a.cell[k] = cell ? double(cell[k]) : 0.0;
   // 2. w-gradient and the per-path dL/dY partials (receiver-major)
-  if (grad_w || grad_pos) CGTP_HIP(launch_bwd_edges(a, s));
+  if (grad_w || grad_pos) CGTP_HIP(launch_bwd_edges(a, P->lmax > 3, s));
   // 3. active slots grouped by sender, then the x-gradient and the forces
   if (grad_x || grad_pos) CGTP_HIP(launch_bwd_transpose(a, ws.t_cnt, ws.t_row_ptr, ws.t_slot, ws.t_recv, s));
-  if (grad_x) CGTP_HIP(launch_bwd_x(a, s));
+  if (grad_x) CGTP_HIP(launch_bwd_x(a, P->lmax > 3, s));
   if (grad_pos) CGTP_HIP(launch_bwd_pos(a, s));
   return ok();
 }

@@ -1,4 +1,5 @@
-// Backward of the CGTP convolution (fp32, plans whose largest l is 3 or less).
+// Backward of the CGTP convolution (fp32, plans whose largest l is kBwdLmax = 4 or less).
+// Built as two translation units: CGTP_BWD_PART 0 holds the edge pass, 1 the rest.
 //
 // LunaTP's abstract puts the derivatives that forces need within the scope of its
 // kernels.  The forward is trilinear in (x_j, w_e, Y(r_e)), so with dL/d out = g:
@@ -26,6 +27,10 @@
 //     node's +/- contributions in slot order.
 #include <hip/hip_runtime.h>
 
+#ifndef CGTP_BWD_PART
+#error "CGTP_BWD_PART must be 0 or 1"
+#endif
+
 #include "launch.hpp"
 #include "sh_eval.hpp"
 #include "variants.hpp"
@@ -34,7 +39,6 @@ namespace cgtp {
 
 namespace {
 
-constexpr int kBwdLmax = 3;
 
 template <int N>
 struct IC {
@@ -52,20 +56,27 @@ __device__ __forceinline__ void sfor(F&& f) {
 template <int L1, int L2, int L3>
 inline constexpr RealCG<L1, L2, L3> kCGb{};
 
-// Runs f(IC<v>) for the variant v of a path: the scalar (K = 1) form of a triple with
-// l <= 3 (the kernels here specialise on (l1, l2, l3) only).
-template <int LO, int HI, typename F>
+// Runs f(IC<v>) for the variant v of a path: the scalar (K = 1) form of a triple whose
+// largest l is at most LMAX (the kernels here specialise on (l1, l2, l3) only).  Each
+// kernel below is built twice, for l <= 3 and for l = 4 paths, so that the registers
+// the l = 4 code needs do not lower the occupancy of the l <= 3 code.
+constexpr int kBwdLowLmax = 3;
+static_assert(kBwdLmax == kBwdLowLmax + 1, "one high instantiation covers l = kBwdLmax");
+
+template <int LO, int HI, int LMAX, typename F>
 __device__ __forceinline__ void by_variant(int v, F&& f) {
   if constexpr (HI - LO == 1) {
-    if constexpr (variant_lmax(LO) <= kBwdLmax && variant_desc(LO).k == 1) f(IC<LO>{});
+    if constexpr (variant_lmax(LO) <= LMAX && variant_desc(LO).k == 1) f(IC<LO>{});
   } else {
     constexpr int MID = (LO + HI) / 2;
     if (v < MID)
-      by_variant<LO, MID>(v, f);
+      by_variant<LO, MID, LMAX>(v, f);
     else
-      by_variant<MID, HI>(v, f);
+      by_variant<MID, HI, LMAX>(v, f);
   }
 }
+
+__device__ __forceinline__ int path_lmax(const PathDev& P) { return max(P.l1, max(P.l2, P.l3)); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -93,6 +104,7 @@ __device__ __forceinline__ void form_a(const float* Y, float (*A)[2 * L3 + 1]) {
   });
 }
 
+#if CGTP_BWD_PART == 0
 // ---------------------------------------------------------------------------------
 // w-gradient and per-path dL/dY
 // ---------------------------------------------------------------------------------
@@ -363,11 +375,14 @@ __device__ __forceinline__ void bwd_edge_path_folded(const BwdArgs& a, const Pat
   }
 }
 
+// HIGH: the instantiation for the l = kBwdLmax paths (the other one skips them)
+template <bool HIGH>
 __global__ void __launch_bounds__(kWave) bwd_edge_kernel(BwdArgs a) {
   __shared__ EdgeLists L;
   const int i = int(blockIdx.x);
   const PathDev P = a.paths[blockIdx.y];
-  by_variant<0, kNumVariants>(P.variant, [&](auto V) {
+  if ((path_lmax(P) > kBwdLowLmax) != HIGH) return;
+  by_variant<0, kNumVariants, HIGH ? kBwdLmax : kBwdLowLmax>(P.variant, [&](auto V) {
     constexpr VariantDesc d = variant_desc(decltype(V)::value);
     // the folded form with one or two 64-channel chunks per walk of the row's edges;
     // paths of more than 64 channels whose folded coupling is too large to hold twice
@@ -381,6 +396,8 @@ __global__ void __launch_bounds__(kWave) bwd_edge_kernel(BwdArgs a) {
       bwd_edge_path_direct<d.l1, d.l2, d.l3>(a, P, i, L);
   });
 }
+
+#else   // CGTP_BWD_PART == 1
 
 // ---------------------------------------------------------------------------------
 // active slots grouped by sender
@@ -530,7 +547,7 @@ __device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, i
   }
 }
 
-template <int L1>
+template <int L1, int LMAX>
 __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
   constexpr int N1 = 2 * L1 + 1;
   const int mul = a.irrep_mul[ir], off = a.irrep_off[ir];
@@ -549,7 +566,7 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
       const int my_e = a.act_e[my_s];
       for (int pp = p0; pp < p1; ++pp) {
         const PathDev P = a.paths[a.irrep_paths[pp]];
-        by_variant<0, kNumVariants>(P.variant, [&](auto V) {
+        by_variant<0, kNumVariants, LMAX>(P.variant, [&](auto V) {
           constexpr VariantDesc d = variant_desc(decltype(V)::value);
           if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, cnt, my_s, my_i, my_e, u, ok, acc);
         });
@@ -562,13 +579,23 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
   }
 }
 
+// HIGH: the instantiation for the input irreps with a path of l = kBwdLmax (all of
+// such an irrep's paths accumulate in one wave's registers)
+template <bool HIGH>
 __global__ void __launch_bounds__(kWave) bwd_x_kernel(BwdArgs a) {
   const int j = int(blockIdx.x), ir = int(blockIdx.y);
+  int lm = 0;
+  for (int pp = a.irrep_start[ir]; pp < a.irrep_start[ir + 1]; ++pp) lm = max(lm, path_lmax(a.paths[a.irrep_paths[pp]]));
+  if ((lm > kBwdLowLmax) != HIGH) return;
+  constexpr int LM = HIGH ? kBwdLmax : kBwdLowLmax;
   switch (a.irrep_l[ir]) {
-    case 0: bwd_x_irrep<0>(a, j, ir); break;
-    case 1: bwd_x_irrep<1>(a, j, ir); break;
-    case 2: bwd_x_irrep<2>(a, j, ir); break;
-    case 3: bwd_x_irrep<3>(a, j, ir); break;
+    case 0: bwd_x_irrep<0, LM>(a, j, ir); break;
+    case 1: bwd_x_irrep<1, LM>(a, j, ir); break;
+    case 2: bwd_x_irrep<2, LM>(a, j, ir); break;
+    case 3: bwd_x_irrep<3, LM>(a, j, ir); break;
+    case 4:
+      if constexpr (HIGH) bwd_x_irrep<4, LM>(a, j, ir);
+      break;
     default: break;
   }
 }
@@ -641,6 +668,7 @@ __global__ void __launch_bounds__(256) bwd_force_kernel(BwdArgs a) {
       case 1: slot_grad_r<1>(a, i, rb + q); break;
       case 2: slot_grad_r<2>(a, i, rb + q); break;
       case 3: slot_grad_r<3>(a, i, rb + q); break;
+      case 4: slot_grad_r<4>(a, i, rb + q); break;
       default:   // l = 0 harmonics only: constant, no gradient
 #pragma unroll
         for (int k = 0; k < 3; ++k) a.grad_r[(long)(rb + q) * 3 + k] = 0.0f;
@@ -678,13 +706,18 @@ __global__ void __launch_bounds__(256) bwd_pos_kernel(BwdArgs a) {
   }
 }
 
+#endif  // CGTP_BWD_PART
+
 }  // namespace
 
-hipError_t launch_bwd_edges(const BwdArgs& a, hipStream_t s) {
+#if CGTP_BWD_PART == 0
+hipError_t launch_bwd_edges(const BwdArgs& a, bool high, hipStream_t s) {
   if (a.n_nodes == 0 || a.n_paths == 0) return hipSuccess;
-  bwd_edge_kernel<<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
+  bwd_edge_kernel<false><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
+  if (high) bwd_edge_kernel<true><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
   return hipGetLastError();
 }
+#else
 
 hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,
                                 int32_t* t_recv, hipStream_t s) {
@@ -701,9 +734,10 @@ hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_x(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s) {
   if (a.n_nodes == 0 || a.n_irreps == 0) return hipSuccess;
-  bwd_x_kernel<<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+  bwd_x_kernel<false><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+  if (high) bwd_x_kernel<true><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -714,5 +748,6 @@ hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s) {
   bwd_pos_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
   return hipGetLastError();
 }
+#endif  // CGTP_BWD_PART
 
 }  // namespace cgtp

@@ -90,16 +90,21 @@ hipError_t launch_conv(const ConvArgsT<float>& args, int cls, hipStream_t s, hip
 hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hipEvent_t ev_start,
                        hipEvent_t ev_stop);
 
-// Backward of the convolution (fp32, plans with l <= 3).  bwd_edges: w-gradient of every
+// Largest l of a plan that the backward supports.
+constexpr int kBwdLmax = 4;
+
+// Backward of the convolution (fp32, plans with l <= kBwdLmax).  bwd_edges: w-gradient of every
 // edge (zero rows for inactive ones) and, when want_gy, the per-path dL/dY partial of
-// every active slot; one wave per (receiver, path).
-hipError_t launch_bwd_edges(const BwdArgs& a, hipStream_t s);
+// every active slot; one wave per (receiver, path).  high: the plan has paths of
+// l = kBwdLmax (they run in a second launch, built apart from the l <= 3 code).
+hipError_t launch_bwd_edges(const BwdArgs& a, bool high, hipStream_t s);
 // Active slots grouped by sender: t_row_ptr [n+1], t_slot / t_recv [active edges], each
 // sender's entries in slot order.  t_cnt: [n] scratch.
 hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,
                                 int32_t* t_recv, hipStream_t s);
-// x-gradient: one wave per (sender, input irrep), all its paths in path order.
-hipError_t launch_bwd_x(const BwdArgs& a, hipStream_t s);
+// x-gradient: one wave per (sender, input irrep), all its paths in path order; high as
+// for the edge pass (irreps with an l = kBwdLmax path run in the second launch).
+hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s);
 // dL/dr per active slot from the partials and dY/dr, then the position gradient.
 hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s);
 

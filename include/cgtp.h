@@ -1,6 +1,6 @@
 /*
  * cgtp.h -- C ABI of libcgtp.so: the Clebsch-Gordan tensor-product (CGTP)
- * convolution, forward (fp32, and fp64 for l <= 3) and gradients (fp32, l <= 3), for
+ * convolution, forward (fp32, and fp64 for l <= 3) and gradients (fp32, l <= 4), for
  * AMD Instinct MI355X (gfx950).
  *
  * What is computed (the pages print no formula; this is the textbook definition that
@@ -218,7 +218,7 @@ int cgtp_backward_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_ed
  *                             dY/dr (forces are -grad_pos when L is an energy).
  * The mask, gate (BranchIP continuation gate; it scales the message and is not
  * differentiated), cell and shifts are constants; inactive edges contribute nothing
- * and their w and x_j are never read.  fp32 plans whose largest l is 3 or less (else
+ * and their w and x_j are never read.  fp32 plans whose largest l is 4 or less (else
  * CGTP_ERR_UNSUPPORTED; an fp64 plan gives CGTP_ERR_INVALID_ARG).  Other arguments as
  * cgtp_conv_forward_gated; 4-byte aligned pointers; workspace at least
  * cgtp_backward_workspace_size.  Asynchronous on `stream`; results are bitwise

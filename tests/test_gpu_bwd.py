@@ -38,7 +38,7 @@ def _rel(got, ref):
     return np.linalg.norm(got - ref) / nref if nref > 0 else np.linalg.norm(got - ref)
 
 
-def _check(got, ref, what):
+def _check(got, ref, what, whole=True):
     gx, gw, gp = (np.asarray(g, dtype=np.float64) for g in got)
     rx, rw, rp = ref
     for g in (gx, gw, gp):
@@ -52,7 +52,9 @@ def _check(got, ref, what):
           f"pos rel {ep:.2e} max/scale {mp:.2e} sum/scale {drift:.2e}", flush=True)
     assert ex <= REL_L2 and mx <= MAX_ABS, (what, "x", ex, mx)
     assert ew <= REL_L2 and mw <= MAX_ABS, (what, "w", ew, mw)
-    assert ep <= REL_L2 and mp <= 1e-4 and drift <= 1e-4, (what, "pos", ep, mp, drift)
+    assert ep <= REL_L2 and mp <= 1e-4, (what, "pos", ep, mp)
+    if whole:   # over all nodes the position gradient sums to zero
+        assert drift <= 1e-4, (what, "pos sum", drift)
 
 
 _CACHE = {}
@@ -89,6 +91,26 @@ def test_backward_workloads(dev, name):
     _check(got, ref, name)
 
 
+@pytest.mark.parametrize("name", ["c5_768", "c6_768"])
+def test_backward_full_size_sampled(dev, name):
+    """LunaTP Table 1 cases 5 and 6 (L = 4) at full size on the GPU.  The oracle takes the
+    edges incident to 12 sampled nodes: the w-gradient of an edge depends on that edge
+    alone, and a node's x- and position gradients on the edges it sends or receives, so
+    on those edges and nodes the sub-graph's gradients are the full graph's."""
+    wl, plan, pos, cell, rp, col, sh, x, w, mask, gate, gout = _workload(name)
+    p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    gx, gw, gp = _gpu_bwd(dev, p, pos, cell, rp, col, sh, x, w, gout)
+    n = len(pos)
+    nodes = np.random.default_rng(5).choice(n, 12, replace=False)
+    recv = np.repeat(np.arange(n), np.diff(rp))
+    keep = np.isin(recv, nodes) | np.isin(col, nodes)
+    eids = np.flatnonzero(keep)
+    rp_sub = np.concatenate([[0], np.cumsum(np.bincount(recv[eids], minlength=n))]).astype(np.int32)
+    rx, rw, rpos = O.conv_backward(plan, pos, cell, rp_sub, col[eids], sh[eids], x, w[eids], gout)
+    got = (gx[nodes], gw[eids], gp[nodes])
+    _check(got, (rx[nodes], rw, rpos[nodes]), f"{name}[{len(nodes)} nodes, {len(eids)} edges]", whole=False)
+
+
 def _small_system(n, box_len, cutoff, seed):
     rng = np.random.default_rng(seed)
     pos = (rng.random((n, 3)) * box_len).astype(np.float32)
@@ -99,18 +121,18 @@ def _small_system(n, box_len, cutoff, seed):
     return rng, pos, cell, rp, col, sh
 
 
-@pytest.mark.parametrize("l1", range(4))
+@pytest.mark.parametrize("l1", range(5))
 @pytest.mark.parametrize("mul", [3, 70])
 def test_backward_every_path(dev, l1, mul):
-    """Every (l1, l2, l3) with l <= 3; 70 channels = two 64-lane chunks, the second ragged."""
+    """Every (l1, l2, l3) with l <= 4; 70 channels = two 64-lane chunks, the second ragged."""
     rng, pos, cell, rp, col, sh = _small_system(36, 6.0, 2.7, 300 + l1)
-    for l2 in range(4):
+    for l2 in range(5):
         spec_in, spec_sh = f"{mul}x{l1}e", f"1x{l2}e"
-        plan = O.build_plan(spec_in, spec_sh, 3, O.PATHS_ALL)
+        plan = O.build_plan(spec_in, spec_sh, 4, O.PATHS_ALL)
         x = rng.standard_normal((len(pos), plan.f_in)).astype(np.float32)
         w = rng.standard_normal((len(col), plan.w_per_edge)).astype(np.float32)
         gout = rng.standard_normal((len(pos), plan.f_out)).astype(np.float32)
-        p = C.Plan(spec_in, spec_sh, 3, "all")
+        p = C.Plan(spec_in, spec_sh, 4, "all")
         got = _gpu_bwd(dev, p, pos, cell, rp, col, sh, x, w, gout)
         ref = O.conv_backward(plan, pos, cell, rp, col, sh, x, w, gout)
         _check(got, ref, f"{spec_in} x {spec_sh}")
@@ -172,7 +194,7 @@ def test_backward_refusals(dev):
     out = torch.empty(n * 3, dtype=torch.float32, device=dev)
     s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     for plan_args, code in [((wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule, False, True), -1),
-                            (("8x0e+8x4e", "1x0e+1x1o", 4, "all"), -3)]:
+                            (("8x0e+8x5e", "1x0e+1x1o", 5, "all"), -3)]:
         p = C.Plan(*plan_args)
         ws = torch.empty(p.backward_workspace_size(n, e), dtype=torch.uint8, device=dev)
         rc = lib.cgtp_conv_backward(p.handle, d(pos_d), n, None, d(rp_d), d(col_d), None, e, d(x_d), d(w_d), None,
