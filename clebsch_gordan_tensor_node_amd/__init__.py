@@ -1,4 +1,4 @@
-"""MI355X-native Clebsch-Gordan tensor-product (CGTP) convolution, forward (fp32; fp64 for l <= 3).
+"""MI355X-native Clebsch-Gordan tensor-product (CGTP) convolution, forward (fp32; fp64 for l <= 4).
 
 Thin binding over libcgtp.so (C ABI in include/cgtp.h): argument marshalling only.
 Every step of the path (neighbour list, mask prepare, edge harmonics, the fused

@@ -510,9 +510,9 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   if (P->elem == 8) {
     int lmax = 0;
     for (const PathInfo& p : P->paths) lmax = std::max(lmax, std::max(p.l1, std::max(p.l2, p.l3)));
-    if (lmax > 3) {
+    if (lmax > kF64Lmax) {
       delete P;
-      return fail(CGTP_ERR_UNSUPPORTED, "fp64 plans support l <= 3 (this plan reaches l = %d)", lmax);
+      return fail(CGTP_ERR_UNSUPPORTED, "fp64 plans support l <= %d (this plan reaches l = %d)", kF64Lmax, lmax);
     }
   }
   P->irreps_out = format_irreps(P->out);

@@ -86,8 +86,10 @@ struct ConvArgsT {
   GroupArgs grp[kMaxGroupsPerLaunch];
 };
 using ConvArgs = ConvArgsT<float>;
-// the kernel classes (l <= 3) that are also built in fp64
-constexpr int kNumClassesF64 = 2;
+// fp64 is built for the variants with l <= kF64Lmax: the kernel classes below
+// kNumClassesF64 (l <= 2, l <= 3, and l1 = 0 .. kF64Lmax of the l >= 4 classes)
+constexpr int kF64Lmax = 4;
+constexpr int kNumClassesF64 = 3 + kF64Lmax;
 
 // One path of a plan, for the backward kernels (device table owned by the plan).
 struct PathDev {

@@ -459,7 +459,7 @@ template <int C, typename T, int LO, int HI>
 __device__ __forceinline__ void dispatch(int v, const ConvArgsT<T>& a, const Job& J, int ng, int lg, int y0, int y4,
                                          int wave, bool has_job, ConvSmem<C, T>& sm) {
   if constexpr (HI - LO == 1) {
-    if constexpr (class_contains(C, LO)) {
+    if constexpr (class_contains(C, LO) && (sizeof(T) == 4 || variant_lmax(LO) <= kF64Lmax)) {
       constexpr VariantDesc d = variant_desc(LO);
       constexpr int K = d.k == 1 ? 1 : kVec<T>;   // the vector form moves 16 bytes per lane
       run_job<C, T, d.l1, d.l2, d.l3, K>(a, J, ng, lg, y0, y4, wave, has_job, sm);

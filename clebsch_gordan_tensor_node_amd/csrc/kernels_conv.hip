@@ -9,7 +9,8 @@
 namespace cgtp {
 template hipError_t launch_conv_class<CGTP_CONV_CLASS, float>(const ConvArgsT<float>& args, hipStream_t s,
                                                               hipEvent_t ev_start, hipEvent_t ev_stop);
-#if CGTP_CONV_CLASS < 2
+#if CGTP_CONV_CLASS < 7   // kNumClassesF64
+static_assert(CGTP_CONV_CLASS < kNumClassesF64, "fp64 class range");
 template hipError_t launch_conv_class<CGTP_CONV_CLASS, double>(const ConvArgsT<double>& args, hipStream_t s,
                                                                hipEvent_t ev_start, hipEvent_t ev_stop);
 #endif

@@ -616,6 +616,7 @@ hipError_t launch_rows(const RowPass& p, int l_sh_max, hipStream_t s) {
       case 1: edge_rows_kernel<1, double><<<nb, kRowThreads, 0, s>>>(a); break;
       case 2: edge_rows_kernel<2, double><<<nb, kRowThreads, 0, s>>>(a); break;
       case 3: edge_rows_kernel<3, double><<<nb, kRowThreads, 0, s>>>(a); break;
+      case 4: edge_rows_kernel<4, double><<<nb, kRowThreads, 0, s>>>(a); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -650,6 +651,7 @@ hipError_t launch_rows_order(const RowPass& p, int l_sh_max, int4* node_info, hi
       case 1: rows_order_kernel<1, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
       case 2: rows_order_kernel<2, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
       case 3: rows_order_kernel<3, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
+      case 4: rows_order_kernel<4, double><<<nb, kScanThreads, 0, s>>>(a, node_info); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -707,10 +709,15 @@ hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hi
   switch (cls) {
     case 0: return launch_conv_class<0, double>(args, s, b, e);
     case 1: return launch_conv_class<1, double>(args, s, b, e);
+    case 2: return launch_conv_class<2, double>(args, s, b, e);
+    case 3: return launch_conv_class<3, double>(args, s, b, e);
+    case 4: return launch_conv_class<4, double>(args, s, b, e);
+    case 5: return launch_conv_class<5, double>(args, s, b, e);
+    case 6: return launch_conv_class<6, double>(args, s, b, e);
     default: return hipErrorInvalidValue;
   }
 }
-static_assert(kNumClassesF64 == 2, "launch_conv covers every fp64 kernel class");
+static_assert(kNumClassesF64 == 7, "launch_conv covers every fp64 kernel class");
 
 static_assert(kNumClasses == 9, "launch_conv covers every kernel class");
 

@@ -1,6 +1,6 @@
 /*
  * cgtp.h -- C ABI of libcgtp.so: the Clebsch-Gordan tensor-product (CGTP)
- * convolution, forward (fp32, and fp64 for l <= 3) and gradients (fp32, l <= 4), for
+ * convolution, forward (fp32, and fp64 for l <= 4) and gradients (fp32, l <= 4), for
  * AMD Instinct MI355X (gfx950).
  *
  * What is computed (the pages print no formula; this is the textbook definition that
@@ -80,7 +80,7 @@ enum { CGTP_PATHS_ALL = 0, CGTP_PATHS_PARITY = 1 };
  * plan answers the query calls but cgtp_conv_* return CGTP_ERR_INVALID_ARG with it.
  * CGTP_PLAN_FP64: the plan's forward runs in fp64 (LunaTP reports its kernels in
  * double precision: Figure 8, Table 11); it is used with cgtp_conv_forward_f64 only,
- * supports l <= 3 (else CGTP_ERR_UNSUPPORTED), and its workspace holds fp64
+ * supports l <= 4 (else CGTP_ERR_UNSUPPORTED), and its workspace holds fp64
  * harmonics.  The fp32 forward entry points return CGTP_ERR_INVALID_ARG with an fp64
  * plan and cgtp_conv_forward_f64 with an fp32 plan. */
 enum { CGTP_PLAN_HOST_ONLY = 1u, CGTP_PLAN_FP64 = 2u };

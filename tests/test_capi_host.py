@@ -120,12 +120,13 @@ def test_fp64_plan_host(name):
 
 
 def test_fp64_plan_limits():
-    with pytest.raises(C.CgtpError) as e:        # fp64 kernels are built for l <= 3
-        C.Plan("8x0e+8x4e", "1x0e+1x1o", 4, "all", host_only=True, fp64=True)
+    with pytest.raises(C.CgtpError) as e:        # fp64 kernels are built for l <= 4
+        C.Plan("8x0e+8x5e", "1x0e+1x1o", 5, "all", host_only=True, fp64=True)
     assert e.value.code == -3
-    with pytest.raises(C.CgtpError) as e:
-        C.Plan("8x1o", "1x0e+1x4e", 3, "all", host_only=True, fp64=True)
+    with pytest.raises(C.CgtpError) as e:        # l = 5 in the harmonics only
+        C.Plan("8x2o", "1x0e+1x5e", 3, "all", host_only=True, fp64=True)
     assert e.value.code == -3
+    C.Plan("8x0e+8x4e", "1x0e+1x4e", 4, "all", host_only=True, fp64=True)
     lib = C._lib.load()
     h = ctypes.c_void_p()
     assert lib.cgtp_plan_create(b"8x0e", b"1x0e", 0, 0, 4, ctypes.byref(h)) == -1   # unknown flag

@@ -94,20 +94,41 @@ def _small_system(n, box_len, cutoff, seed):
     return rng, pos, box, cell, rp, col, sh
 
 
-@pytest.mark.parametrize("l1", range(4))
+@pytest.mark.parametrize("l1", range(5))
 @pytest.mark.parametrize("mul", [2, 3, 130])
 def test_conv_f64_every_variant(dev, l1, mul):
-    """Every (l1, l2, l3) with l <= 3 in fp64: K = 2 (mul 2; mul 130 = one full channel
+    """Every (l1, l2, l3) with l <= 4 in fp64: K = 2 (mul 2; mul 130 = one full channel
     block of 64 lanes * 2 and a ragged one) and K = 1 (mul 3)."""
     rng, pos, box, cell, rp, col, sh = _small_system(40, 6.0, 2.6, 200 + l1)
-    for l2 in range(4):
+    for l2 in range(5):
         spec_in, spec_sh = f"{mul}x{l1}e", f"1x{l2}e"
-        plan = O.build_plan(spec_in, spec_sh, 3, O.PATHS_ALL)
+        plan = O.build_plan(spec_in, spec_sh, 4, O.PATHS_ALL)
         x = rng.standard_normal((len(pos), plan.f_in))
         w = rng.standard_normal((len(col), plan.w_per_edge))
-        got = _gpu_conv64(dev, (spec_in, spec_sh, 3, "all"), pos, cell, rp, col, sh, x, w)
+        got = _gpu_conv64(dev, (spec_in, spec_sh, 4, "all"), pos, cell, rp, col, sh, x, w)
         ref = O.conv_forward(plan, pos.astype(np.float64), cell, rp, col, sh, x, w)
         _compare(got, ref, f"{spec_in} x {spec_sh} fp64")
+
+
+@pytest.mark.parametrize("name", ["c5_768", "c6_768"])
+def test_conv_f64_sampled_large(dev, name):
+    # LunaTP Table 1 cases 5 and 6 (L = 4) in fp64 at full size; the oracle evaluates 48
+    # sampled receivers on the sub-graph of their rows (senders keep their ids)
+    wl, plan, pos, box, cell, rp, col, sh, x, w, mask, gate = _workload(name)
+    spec = (wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
+    got = _gpu_conv64(dev, spec, pos, cell, rp, col, sh, x, w)
+    rows = np.random.default_rng(1).choice(wl.n_atoms, 48, replace=False)
+    segs = [np.arange(rp[i], rp[i + 1]) for i in rows]
+    eids = np.concatenate(segs)
+    srp = np.concatenate([[0], np.cumsum([len(s) for s in segs])])
+    n = wl.n_atoms
+    pos_sub = np.concatenate([pos[rows], pos]).astype(np.float64)
+    col_sub = (col[eids] + len(rows)).astype(np.int32)
+    x_sub = np.concatenate([x[rows], x]).astype(np.float64)
+    rp_full = np.concatenate([srp, np.full(n, srp[-1])]).astype(np.int32)
+    ref = O.conv_forward(plan, pos_sub, cell, rp_full, col_sub, sh[eids], x_sub, w[eids].astype(np.float64),
+                         None)[:len(rows)]
+    _compare(got[rows], ref, f"{name}[48 rows] fp64")
 
 
 def test_conv_f64_deterministic(dev):
