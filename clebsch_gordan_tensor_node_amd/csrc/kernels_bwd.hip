@@ -21,7 +21,9 @@
 //     dL/dY over the lanes with a fixed butterfly;
 //   * the active slots are regrouped by sender (counts, scan, placement, per-sender sort
 //     by slot), so that the x-gradient is a gather: bwd_x_kernel runs one wave per
-//     (sender, input irrep) and accumulates all of that irrep's paths in registers;
+//     (sender, input irrep) and accumulates all of that irrep's paths in registers
+//     (an irrep of 32 channels or fewer runs 64 / 2^ceil(log2 mul) of the sender's
+//     edges side by side and adds the partial sums by a fixed butterfly);
 //   * bwd_force_kernel evaluates dY/dr by running the harmonics' recurrence on dual
 //     numbers (exact derivatives of the same polynomials), and bwd_pos_kernel sums each
 //     node's +/- contributions in slot order.
@@ -507,18 +509,21 @@ __global__ void __launch_bounds__(kWave) bwd_t_sort_kernel(const int32_t* t_row_
 // ---------------------------------------------------------------------------------
 
 // entries k0 .. k0 + cnt - 1 of the sender's list: slot, receiver and edge id of entry
-// k0 + lane are held by that lane
+// k0 + lane are held by that lane.  The lanes form nsub sub-groups (sub = this lane's):
+// sub-group g takes entries g, g + nsub, ... (uniform trip count, idle at the tail).
 template <int L1, int L2, int L3>
-__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int cnt, int my_s, int my_i,
-                                           int my_e, int u, bool ok, float* acc) {
+__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int cnt, int sub, int nsub,
+                                           int my_s, int my_i, int my_e, int u, bool ok, float* acc) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  // one-deep pipeline: entry k + 1's harmonics, weight and grad_out rows are loaded
-  // (at a clamped index, unconditionally) while entry k is used
+  // D-deep pipeline: the harmonics, weight and grad_out rows of the next D entries of
+  // this sub-group are in flight (loaded at clamped indices, unconditionally) while one
+  // entry is used; D from the registers an entry holds
   struct Entry {
     float Y[N2];
     float w;
     float go[N3];
   };
+  constexpr int D = 48 / (N2 + 1 + N3) < 2 ? 2 : (48 / (N2 + 1 + N3) > 4 ? 4 : 48 / (N2 + 1 + N3));
   const int uu = ok ? u : 0;
   auto load = [&](int k, Entry& d) {
     const int s = __shfl(my_s, k, kWave), i = __shfl(my_i, k, kWave), e = __shfl(my_e, k, kWave);
@@ -528,20 +533,29 @@ __device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, i
 #pragma unroll
     for (int m = 0; m < N3; ++m) d.go[m] = a.grad_out[(long)i * a.f_out + P.out_off + uu * N3 + m];
   };
-  Entry cur, nxt;
-  load(0, nxt);
-  for (int k = 0; k < cnt; ++k) {
-    cur = nxt;
-    load(min(k + 1, cnt - 1), nxt);
-    float A[N1][N3];
-    form_a<L1, L2, L3>(cur.Y, A);
-    if (ok) {
+  const int steps = (cnt + nsub - 1) / nsub;
+  Entry ring[D];
 #pragma unroll
-      for (int m1 = 0; m1 < N1; ++m1) {
-        float t = 0.0f;
+  for (int r = 0; r < D; ++r) load(min(sub + r * nsub, cnt - 1), ring[r]);
+  for (int t0 = 0; t0 < steps; t0 += D) {
 #pragma unroll
-        for (int m3 = 0; m3 < N3; ++m3) t = __builtin_fmaf(A[m1][m3], cur.go[m3], t);
-        acc[m1] = __builtin_fmaf(cur.w, t, acc[m1]);
+    for (int r = 0; r < D; ++r) {
+      const int t = t0 + r;
+      if (t < steps) {   // uniform over the wave
+        const int k = t * nsub + sub;
+        const Entry cur = ring[r];
+        load(min(k + D * nsub, cnt - 1), ring[r]);
+        float A[N1][N3];
+        form_a<L1, L2, L3>(cur.Y, A);
+        if (ok && k < cnt) {
+#pragma unroll
+          for (int m1 = 0; m1 < N1; ++m1) {
+            float v = 0.0f;
+#pragma unroll
+            for (int m3 = 0; m3 < N3; ++m3) v = __builtin_fmaf(A[m1][m3], cur.go[m3], v);
+            acc[m1] = __builtin_fmaf(cur.w, v, acc[m1]);
+          }
+        }
       }
     }
   }
@@ -552,8 +566,14 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
   constexpr int N1 = 2 * L1 + 1;
   const int mul = a.irrep_mul[ir], off = a.irrep_off[ir];
   const int p0 = a.irrep_start[ir], p1 = a.irrep_start[ir + 1];
+  // lanes per entry: the next power of two of the multiplicity, at most 64; the
+  // 64 / cw sub-groups of a wave walk interleaved entries of the sender's list and their
+  // partial sums are added by a fixed butterfly before the store
+  int cw = 1;
+  while (cw < mul && cw < kWave) cw <<= 1;
+  const int lane = int(threadIdx.x), sub = lane / cw, nsub = kWave / cw;
   for (int u0 = 0; u0 < mul; u0 += kWave) {
-    const int u = u0 + int(threadIdx.x);
+    const int u = u0 + (lane & (cw - 1));
     const bool ok = u < mul;
     float acc[N1];
 #pragma unroll
@@ -568,11 +588,15 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
         const PathDev P = a.paths[a.irrep_paths[pp]];
         by_variant<0, kNumVariants, LMAX>(P.variant, [&](auto V) {
           constexpr VariantDesc d = variant_desc(decltype(V)::value);
-          if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, cnt, my_s, my_i, my_e, u, ok, acc);
+          if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, cnt, sub, nsub, my_s, my_i, my_e, u, ok, acc);
         });
       }
     }
-    if (ok) {
+    for (int d = cw; d < kWave; d <<= 1) {
+#pragma unroll
+      for (int m = 0; m < N1; ++m) acc[m] += __shfl_xor(acc[m], d, kWave);
+    }
+    if (ok && sub == 0) {
 #pragma unroll
       for (int m = 0; m < N1; ++m) a.grad_x[(long)j * a.f_in + off + u * N1 + m] = acc[m];
     }
