@@ -163,6 +163,7 @@ struct cgtp_plan_s {
   std::vector<PathDev> pdev;
   std::vector<int32_t> irrep_tab;
   int gy_stride = 0;                 // sum over paths of 2 l2 + 1
+  int xp_stride = 0;                 // sum over paths of mul (2 l1 + 1)
   int lmax = 0;                      // largest l of the plan
   PathDev* d_paths = nullptr;
   int32_t* d_irrep = nullptr;
@@ -519,6 +520,7 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   schedule(*P);
   // backward tables
   P->gy_stride = 0;
+  P->xp_stride = 0;
   P->lmax = 0;
   for (const PathInfo& p : P->paths) {
     PathDev d{};
@@ -533,7 +535,9 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     d.sh_off = p.l2 * p.l2;
     d.gy_off = P->gy_stride;
     d.i_in = p.i_in;
+    d.xp_off = P->xp_stride;
     P->gy_stride += 2 * p.l2 + 1;
+    P->xp_stride += p.mul * (2 * p.l1 + 1);
     P->lmax = std::max(P->lmax, std::max(p.l1, std::max(p.l2, p.l3)));
     P->pdev.push_back(d);
   }
@@ -945,7 +949,7 @@ int cgtp_conv_forward_f64(cgtp_plan_t P, const double* pos, int64_t n_nodes, con
 struct BwdWorkspace {
   FwdWorkspace fwd;
   int32_t *t_cnt, *t_row_ptr, *t_slot, *t_recv;
-  float *gyp, *grad_r;
+  float *gyp, *grad_r, *xp;
   size_t bytes;
 };
 
@@ -965,6 +969,7 @@ static BwdWorkspace carve_bwd(const cgtp_plan_s& P, int64_t n, int64_t e, void* 
   w.t_recv = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.gyp = reinterpret_cast<float*>(take(size_t(e) * size_t(P.gy_stride) * 4));
   w.grad_r = reinterpret_cast<float*>(take(size_t(e) * 12));
+  w.xp = reinterpret_cast<float*>(take(size_t(n) * size_t(P.xp_stride) * 4));
   w.bytes = off;
   return w;
 }
@@ -1044,6 +1049,8 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   a.grad_w = grad_w;
   a.gyp = ws.gyp;
   a.grad_r = ws.grad_r;
+  a.xp = ws.xp;
+  a.xp_stride = P->xp_stride;
   a.grad_pos = grad_pos;
   a.n_nodes = int(n_nodes);
   a.n_paths = np;

@@ -100,7 +100,7 @@ struct PathDev {
   int32_t sh_off;      // l2 * l2: the path's harmonics within an SH row
   int32_t gy_off;      // the path's block within a row of per-path dL/dY partials
   int32_t i_in;        // input irrep index
-  int32_t pad;
+  int32_t xp_off;      // the path's block within a row of per-path x-gradient partials
 };
 
 // Arguments of the backward kernels (fp32).  Active slots are those of the forward's
@@ -130,11 +130,12 @@ struct BwdArgs {
   float* grad_x;
   float* grad_w;
   float* gyp;                 // [slot, gy_stride] per-path dL/dY partials
+  float* xp;                  // [node, xp_stride] per-path x-gradient partials
   float* grad_r;              // [slot, 3] dL/dr
   float* grad_pos;
   int32_t n_nodes, n_paths, n_irreps;
   int32_t f_in, f_out, w_stride, sh_stride, gy_stride, l_sh_max;
-  int32_t want_gy, has_cell;
+  int32_t want_gy, has_cell, xp_stride;
   double cell[9];
 };
 

@@ -20,10 +20,13 @@
 //     the active ones with a one-deep load pipeline, writes their w-gradient and reduces
 //     dL/dY over the lanes with a fixed butterfly;
 //   * the active slots are regrouped by sender (counts, scan, placement, per-sender sort
-//     by slot), so that the x-gradient is a gather: bwd_x_kernel runs one wave per
-//     (sender, input irrep) and accumulates all of that irrep's paths in registers
-//     (an irrep of 32 channels or fewer runs 64 / 2^ceil(log2 mul) of the sender's
-//     edges side by side and adds the partial sums by a fixed butterfly);
+//     by slot), so that the x-gradient is a gather: on large graphs bwd_x_kernel runs
+//     one wave per (sender, input irrep) and accumulates all of the irrep's paths in
+//     registers; on graphs too small to fill the chip that way bwd_xp_kernel runs one
+//     wave per (sender, path) and writes that path's partial, and bwd_x_sum_kernel adds
+//     each input irrep's partials in path order (either way a path of 32 channels or
+//     fewer puts several of the sender's edges side by side in one wave and adds their
+//     sums by a fixed butterfly);
 //   * bwd_force_kernel evaluates dY/dr by running the harmonics' recurrence on dual
 //     numbers (exact derivatives of the same polynomials), and bwd_pos_kernel sums each
 //     node's +/- contributions in slot order.
@@ -603,8 +606,9 @@ __device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
   }
 }
 
-// HIGH: the instantiation for the input irreps with a path of l = kBwdLmax (all of
-// such an irrep's paths accumulate in one wave's registers)
+// One wave per (sender, input irrep), all of the irrep's paths accumulated in registers
+// and stored once (no partials).  HIGH: the instantiation for the input irreps with a
+// path of l = kBwdLmax.
 template <bool HIGH>
 __global__ void __launch_bounds__(kWave) bwd_x_kernel(BwdArgs a) {
   const int j = int(blockIdx.x), ir = int(blockIdx.y);
@@ -622,6 +626,62 @@ __global__ void __launch_bounds__(kWave) bwd_x_kernel(BwdArgs a) {
       break;
     default: break;
   }
+}
+
+// One wave per (sender, path): the path's x-gradient partial of every channel of the
+// sender, over its entries in slot order, written to the path's block of the sender's
+// row of partials.  A path of 32 channels or fewer runs 64 / 2^ceil(log2 mul) of the
+// sender's entries side by side and adds the sub-groups' sums by a fixed butterfly.
+template <bool HIGH>
+__global__ void __launch_bounds__(kWave) bwd_xp_kernel(BwdArgs a) {
+  const int j = int(blockIdx.x);
+  const PathDev P = a.paths[blockIdx.y];
+  if ((path_lmax(P) > kBwdLowLmax) != HIGH) return;
+  int cw = 1;
+  while (cw < P.mul && cw < kWave) cw <<= 1;
+  const int lane = int(threadIdx.x), sub = lane / cw, nsub = kWave / cw;
+  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
+  by_variant<0, kNumVariants, HIGH ? kBwdLmax : kBwdLowLmax>(P.variant, [&](auto V) {
+    constexpr VariantDesc d = variant_desc(decltype(V)::value);
+    constexpr int N1 = 2 * d.l1 + 1;
+    for (int u0 = 0; u0 < P.mul; u0 += kWave) {
+      const int u = u0 + (lane & (cw - 1));
+      const bool ok = u < P.mul;
+      float acc[N1];
+#pragma unroll
+      for (int m = 0; m < N1; ++m) acc[m] = 0.0f;
+      for (int k0 = tb; k0 < te; k0 += kWave) {
+        const int cnt = min(kWave, te - k0);
+        const int kk = k0 + min(lane, cnt - 1);
+        const int my_s = a.t_slot[kk], my_i = a.t_recv[kk];
+        const int my_e = a.act_e[my_s];
+        bwd_x_path<d.l1, d.l2, d.l3>(a, P, cnt, sub, nsub, my_s, my_i, my_e, u, ok, acc);
+      }
+      for (int dd = cw; dd < kWave; dd <<= 1) {
+#pragma unroll
+        for (int m = 0; m < N1; ++m) acc[m] += __shfl_xor(acc[m], dd, kWave);
+      }
+      if (ok && sub == 0) {
+#pragma unroll
+        for (int m = 0; m < N1; ++m) a.xp[(long)j * a.xp_stride + P.xp_off + u * N1 + m] = acc[m];
+      }
+    }
+  });
+}
+
+// x-gradient: per node and input-feature column, the partials of the column's irrep's
+// paths added in path order (an irrep without paths gets 0)
+__global__ void __launch_bounds__(256) bwd_x_sum_kernel(BwdArgs a) {
+  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= long(a.n_nodes) * a.f_in) return;
+  const int j = int(idx / a.f_in), c = int(idx - long(j) * a.f_in);
+  int ir = 0;
+  while (ir + 1 < a.n_irreps && a.irrep_off[ir + 1] <= c) ++ir;
+  const int r = c - a.irrep_off[ir];
+  float v = 0.0f;
+  for (int pp = a.irrep_start[ir]; pp < a.irrep_start[ir + 1]; ++pp)
+    v += a.xp[(long)j * a.xp_stride + a.paths[a.irrep_paths[pp]].xp_off + r];
+  a.grad_x[idx] = v;
 }
 
 // ---------------------------------------------------------------------------------
@@ -760,8 +820,21 @@ hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row
 
 hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s) {
   if (a.n_nodes == 0 || a.n_irreps == 0) return hipSuccess;
-  bwd_x_kernel<false><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
-  if (high) bwd_x_kernel<true><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+  // With enough (sender, irrep) waves to fill the chip (4 per SIMD) each wave takes a
+  // whole irrep; otherwise one wave per (sender, path) and a fixed-order sum, which
+  // shortens each wave's chain of dependent loads at the price of the partials' traffic.
+  constexpr long kFillWaves = 4L * 1024;
+  if (long(a.n_nodes) * a.n_irreps >= kFillWaves) {
+    bwd_x_kernel<false><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+    if (high) bwd_x_kernel<true><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  if (a.n_paths > 0) {
+    bwd_xp_kernel<false><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
+    if (high) bwd_xp_kernel<true><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
+  }
+  const long total = long(a.n_nodes) * a.f_in;
+  bwd_x_sum_kernel<<<int((total + 255) / 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

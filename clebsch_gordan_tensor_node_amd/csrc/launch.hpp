@@ -102,8 +102,9 @@ hipError_t launch_bwd_edges(const BwdArgs& a, bool high, hipStream_t s);
 // sender's entries in slot order.  t_cnt: [n] scratch.
 hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,
                                 int32_t* t_recv, hipStream_t s);
-// x-gradient: one wave per (sender, input irrep), all its paths in path order; high as
-// for the edge pass (irreps with an l = kBwdLmax path run in the second launch).
+// x-gradient: one wave per (sender, input irrep) when those waves fill the chip, else
+// per-path partials (one wave per (sender, path)) and their sum per input irrep in path
+// order; high as for the edge pass (the l = kBwdLmax paths run in a second launch).
 hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s);
 // dL/dr per active slot from the partials and dY/dr, then the position gradient.
 hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s);
