@@ -894,20 +894,22 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
     CGTP_HIP(hipEventRecord(P->fork, s));
     for (int k = 0; k < P->n_aux; ++k) CGTP_HIP(hipStreamWaitEvent(P->aux[k], P->fork, 0));
   }
-  for (size_t li = 0; li < launches.size(); ++li) {
+  hipError_t launch_err = hipSuccess;
+  for (size_t li = 0; li < launches.size() && launch_err == hipSuccess; ++li) {
     const auto& L = launches[li];
     fill(L);
     hipStream_t ls = L.stream == 0 ? s : P->aux[L.stream - 1];
-    CGTP_HIP(launch_conv(a, L.cls, ls, !forked && li == 0 ? ev_begin : nullptr,
-                         !forked && li + 1 == launches.size() ? ev_end : nullptr));
+    launch_err = launch_conv(a, L.cls, ls, !forked && li == 0 ? ev_begin : nullptr,
+                             !forked && li + 1 == launches.size() ? ev_end : nullptr);
   }
-  if (forked) {
+  if (forked) {   // joined even after a failed launch, so that `stream` follows what ran
     for (int k = 0; k < P->n_aux; ++k) {
       CGTP_HIP(hipEventRecord(P->join[k], P->aux[k]));
       CGTP_HIP(hipStreamWaitEvent(s, P->join[k], 0));
     }
     if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));
   }
+  CGTP_HIP(launch_err);
   if (launches.empty()) {  // no wave task (cannot happen with n_nodes > 0): keep the events valid
     if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
     if (ev_end) CGTP_HIP(hipEventRecord(ev_end, s));
