@@ -323,6 +323,23 @@ def test_conv_gated(dev):
     _compare(got, O.conv_forward(plan, pos, cell, rp, col, sh, x, w, m, g), "tiny mask+gate")
 
 
+def test_conv_multi_launch_masked_gated(dev):
+    # a plan with several kernel classes (l <= 3, and l = 4 with l1 = 0, 1, 4), so that
+    # its launches fork to the plan's streams, with mask and gate together
+    rng, pos, box, cell, rp, col, sh = _small_system(48, 6.5, 2.8, 21)
+    spec_in, spec_sh = "12x0e+8x1o+4x4e", "1x0e+1x1o+1x4e"
+    plan = O.build_plan(spec_in, spec_sh, 4, O.PATHS_PARITY)
+    x = rng.standard_normal((len(pos), plan.f_in)).astype(np.float32)
+    w = rng.standard_normal((len(col), plan.w_per_edge)).astype(np.float32)
+    m = (rng.random(len(col)) < 0.75).astype(np.uint8)
+    g = np.where(rng.random(len(col)) < 0.25, 0.0, rng.random(len(col))).astype(np.float32)
+    p = C.Plan(spec_in, spec_sh, 4, "parity")
+    got = C.conv_forward(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev), _t(x, dev), _t(w, dev),
+                         _t(m, dev), gate=_t(g, dev))
+    torch.cuda.synchronize()
+    _compare(got.cpu().numpy(), O.conv_forward(plan, pos, cell, rp, col, sh, x, w, m, g), "multi-launch mask+gate")
+
+
 def test_conv_rejects_x_of_4gib(dev):
     # the kernel addresses x with 32-bit byte offsets; the host refuses larger x before
     # any launch (nothing is read from the undersized buffers below)
