@@ -113,7 +113,7 @@ def main(argv=None) -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE {world}); "
-              "the multi-GPU sharding is described in DESIGN.md and not run.", file=sys.stderr)
+              "sharding by receiver rows over several GPUs is not built.", file=sys.stderr)
         return 2
 
     import numpy as np
