@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import argparse
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -49,16 +50,24 @@ def _units():
     return units
 
 
+_INCLUDE = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def _deps(path: str, seen: set) -> set:
+    """The file and every local header it includes, transitively."""
+    path = os.path.normpath(path)
+    if path in seen or not os.path.exists(path):
+        return seen
+    seen.add(path)
+    with open(path) as f:
+        for inc in _INCLUDE.findall(f.read()):
+            _deps(os.path.join(os.path.dirname(path), inc), seen)
+    return seen
+
+
 def _newest_input(src: str) -> float:
-    """Newest modification time among a unit's source, every header and the C ABI."""
-    t = os.path.getmtime(os.path.join(CSRC, src))
-    for f in os.listdir(CSRC):
-        if f.endswith(".hpp"):
-            t = max(t, os.path.getmtime(os.path.join(CSRC, f)))
-    inc = os.path.join(ROOT, "include")
-    for f in os.listdir(inc):
-        t = max(t, os.path.getmtime(os.path.join(inc, f)))
-    return t
+    """Newest modification time among a unit's source and the headers it includes."""
+    return max(os.path.getmtime(f) for f in _deps(os.path.join(CSRC, src), set()))
 
 
 def build(incremental: bool = False, jobs: int | None = None, verbose: bool = True) -> str:
@@ -81,8 +90,13 @@ def build(incremental: bool = False, jobs: int | None = None, verbose: bool = Tr
         return out, time.time() - t0, msgs
 
     t0 = time.time()
+    # the slowest units (the backward's edge pass, the l >= 4 conv classes) start first
+    slow = {"kernels_bwd_p0.o": 0, "kernels_conv_c6.o": 1, "kernels_conv_c7.o": 2, "kernels_conv_c8.o": 3,
+            "kernels_conv_c1.o": 4, "kernels_bwd_p1.o": 5, "kernels_conv_c5.o": 6}
+    order = sorted(range(len(_units())), key=lambda k: slow.get(_units()[k][2], 99))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(compile_one, _units()))
+        done = dict(zip(order, ex.map(compile_one, [_units()[k] for k in order])))
+    results = [done[k] for k in range(len(_units()))]
     objs = [r[0] for r in results]
     if verbose:
         for (src, defs, obj), (_, dt, msgs) in zip(_units(), results):

@@ -5,10 +5,11 @@
 // and stores each output once; (b) paths are grouped and mapped to SIMD lanes by
 // channel block; (c) products are reused and equal coefficients factored; Table 8:
 // inputs shared across paths.  This is the gfx950 design, not a translation:
-//   * a workgroup of 4 waves serves one group (up to 4 paths of one input irrep and
+//   * a workgroup of 4 waves serves one group (up to 3 paths of one input irrep and
 //     channel block) on S consecutive receivers of the degree-sorted order (LunaTP
-//     Table 9: descending degree first); wave p runs path p with T = 64 / S lanes per
-//     receiver, each lane owning K channels;
+//     Table 9: descending degree first): waves 0-2 are consumers, wave p running path p
+//     with T = 64 / S lanes per receiver, each lane owning K channels, and wave 3 is the
+//     producer that gathers the operands the paths share;
 //   * the receivers' active edges are walked in lock step, one edge per receiver per
 //     step.  Per step the workgroup gathers the senders' x_j segments and the edges'
 //     harmonics once, each thread one 16-byte share, into a double-buffered LDS stage;
@@ -30,8 +31,8 @@
 //
 // This header is compiled once per kernel class (kernels_conv.hip with
 // CGTP_CONV_CLASS = 0 .. kNumClasses-1); each build instantiates the class's conv_kernel
-// for fp32 and, for the classes with l <= 3, for fp64 (T = double: the same design with
-// 16-byte chunks of two elements).
+// for fp32 and, for the classes whose variants reach l <= 4, for fp64 (T = double: the
+// same design with 16-byte chunks of two elements).
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -263,8 +264,13 @@ __device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int
   const int srow = (1 << cap_log2) + 1;             // stage row stride
 
   __syncthreads();   // the receiver records (stored by the kernel entry) are visible
-  // the node order is by active degree, descending: the first receiver has the most edges
-  const int qmax = __builtin_amdgcn_readfirstlane(sm.slot[0].z);
+  // the edge steps of the node group: the largest active degree among its S receivers.
+  // The node order is descending only up to its top bin (degrees past the bin count
+  // share one bin in any order), so the first record is not always the largest.
+  int qmax = lane < S ? sm.slot[lane].z : 0;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) qmax = max(qmax, __shfl_xor(qmax, o, kWave));
+  qmax = __builtin_amdgcn_readfirstlane(qmax);
 
   // stage the element offsets of every (receiver, step) of a window; a step past the
   // receiver's last edge repeats that edge, a receiver with no edge uses zeros

@@ -153,6 +153,23 @@ def test_backward_several_irreps_one_l(dev):
     _check(got, O.conv_backward(plan, pos, cell, rp, col, sh, x, w, gout, mask), "mixed irreps, masked")
 
 
+def test_backward_l4_whole_irrep_waves(dev):
+    """A plan reaching l = 4 on a graph large enough (senders times input irreps >= 4096)
+    that the x-gradient runs one wave per (sender, input irrep), the l = 4 paths in their
+    own launch; 70 channels at l = 4 make two chunks, the second ragged."""
+    rng, pos, cell, rp, col, sh = _small_system(840, (840 / 0.05) ** (1 / 3), 3.2, 91)
+    spec_in, spec_sh = "16x0e+8x1o+8x2e+4x3o+70x4e", "1x0e+1x1o+1x2e+1x3o+1x4e"
+    plan = O.build_plan(spec_in, spec_sh, 4, O.PATHS_PARITY)
+    assert len(pos) * len(plan.irreps_in) >= 4096
+    x = rng.standard_normal((len(pos), plan.f_in)).astype(np.float32)
+    w = rng.standard_normal((len(col), plan.w_per_edge)).astype(np.float32)
+    gout = rng.standard_normal((len(pos), plan.f_out)).astype(np.float32)
+    mask = (rng.random(len(col)) < 0.8).astype(np.uint8)
+    p = C.Plan(spec_in, spec_sh, 4, "parity")
+    got = _gpu_bwd(dev, p, pos, cell, rp, col, sh, x, w, gout, mask)
+    _check(got, O.conv_backward(plan, pos, cell, rp, col, sh, x, w, gout, mask), "l = 4, whole-irrep waves")
+
+
 def test_backward_deterministic_and_nan_safe(dev):
     wl, plan, pos, cell, rp, col, sh, x, w, mask, gate, gout = _workload("si_mask")
     p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
