@@ -28,7 +28,7 @@ EXPORTED = [
     "cgtp_plan_create", "cgtp_plan_info", "cgtp_plan_paths", "cgtp_plan_cg", "cgtp_plan_schedule",
     "cgtp_workspace_size", "cgtp_neighbors_workspace_size", "cgtp_neighbors_build",
     "cgtp_conv_prepare", "cgtp_edge_sh", "cgtp_conv_forward", "cgtp_conv_forward_gated", "cgtp_conv_forward_timed",
-    "cgtp_conv_forward_f64", "cgtp_backward_workspace_size", "cgtp_conv_backward", "cgtp_plan_destroy",
+    "cgtp_conv_forward_f64", "cgtp_conv_forward_noalloc", "cgtp_backward_workspace_size", "cgtp_conv_backward", "cgtp_plan_destroy",
     "cgtp_last_error", "cgtp_version",
 ]
 
@@ -74,6 +74,7 @@ def load():
         "cgtp_conv_forward_gated": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P, SZ, P], I32),
         "cgtp_conv_forward_timed": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P, SZ, P, P, P], I32),
         "cgtp_conv_forward_f64": ([P, P, I64, DP, P, P, P, I64, P, P, P, P, P, P, SZ, P, P, P], I32),
+        "cgtp_conv_forward_noalloc": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P], I32),
         "cgtp_backward_workspace_size": ([P, I64, I64, ctypes.POINTER(SZ)], I32),
         "cgtp_conv_backward": ([P, P, I64, FP, P, P, P, I64, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "cgtp_plan_destroy": ([P], None),

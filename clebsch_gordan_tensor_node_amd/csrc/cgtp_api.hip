@@ -946,6 +946,51 @@ int cgtp_conv_forward_f64(cgtp_plan_t P, const double* pos, int64_t n_nodes, con
 
 }  // extern "C"
 
+// Scratch of the no-allocation forward: one copy of this array per GPU, held until the
+// process ends.  Host code never uses its name as an address (in host code the name is
+// a host-side stand-in): kernels and copies get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[CGTP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};   // device address of `scratch`, per device
+
+// The current device's address of `scratch` (the plan's device, already checked to be
+// current).
+int scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(CGTP_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CGTP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return CGTP_OK;
+}
+}  // namespace
+
+extern "C" int cgtp_conv_forward_noalloc(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float cell[9],
+                                         const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
+                                         int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
+                                         const float* gate, float* out, void* stream) {
+  int rc = check_graph_args(P, n_nodes, n_edges, row_ptr);
+  if (rc != CGTP_OK) return rc;
+  const size_t need = carve(*P, n_nodes, n_edges, nullptr).bytes;
+  if (need > CGTP_NOALLOC_SCRATCH_BYTES)
+    return fail(CGTP_ERR_WORKSPACE, "this graph needs %zu bytes of scratch; the no-allocation forward has %zu",
+                need, size_t(CGTP_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  rc = scratch_address(P->device, &ws);
+  if (rc != CGTP_OK) return rc;
+  return conv_forward_impl<float>(P, pos, n_nodes, cell, row_ptr, col, shift, n_edges, x, w, mask, gate, out, ws,
+                                  CGTP_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
+}
+
 // Workspace of the backward: the forward's sections, then the sender-grouped slots, the
 // per-path dL/dY partials and dL/dr per slot.
 struct BwdWorkspace {

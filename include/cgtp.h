@@ -205,6 +205,30 @@ int cgtp_conv_forward_f64(cgtp_plan_t plan, const double* pos, int64_t n_nodes, 
                           const double* gate, double* out, void* workspace, size_t ws_bytes,
                           void* stream, void* ev_conv_begin, void* ev_conv_end);
 
+/* Size of the device scratch array that cgtp_conv_forward_noalloc uses in place of a
+ * workspace: 64 MiB per GPU (for fp32 plans with edge harmonics up to l = 3, about
+ * 900 000 edges). */
+#define CGTP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* cgtp_conv_forward_gated without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  The kernels' scratch (per-row active
+ * degrees, node records, the compacted active edges and their harmonics) lives in a
+ * device array of CGTP_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends; its address is looked up once per device, on the first
+ * call.  Graphs whose scratch (cgtp_workspace_size of the same plan and sizes) exceeds
+ * the array are refused with CGTP_ERR_WORKSPACE before any launch.  Every call on one
+ * GPU shares that GPU's array, and no part of it needs to start at zero: every value a
+ * call reads was written by the same call.  Calls that overlap on one GPU (on streams
+ * that are not ordered with respect to each other) race on the array; calls in stream
+ * order do not.  The caller still allocates x, w, out and the other arguments.  fp32
+ * plans only (an fp64 plan gives CGTP_ERR_INVALID_ARG); results are bitwise those of
+ * cgtp_conv_forward_gated on the same inputs. */
+int cgtp_conv_forward_noalloc(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
+                              const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
+                              int64_t n_edges, const float* x, const float* w, const uint8_t* mask,
+                              const float* gate, float* out, void* stream);
+
 /* Workspace bytes that cgtp_conv_backward needs for this graph size (alignment 256). */
 int cgtp_backward_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, size_t* bytes);
 
