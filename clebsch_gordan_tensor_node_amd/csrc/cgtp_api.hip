@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -14,12 +15,33 @@
 
 #include "../../include/cgtp.h"
 #include "launch.hpp"
+#include "nbr.hpp"
 #include "variants.hpp"
 
 namespace cgtp {
 namespace {
 
 thread_local std::string g_last_error;
+
+// CGTP_LOG in the environment: 1 copies every failing call's message to stderr, 2 adds
+// a line per created plan (paths, jobs, groups, launches and their streams).
+int log_level() {
+  static const int level = [] {
+    const char* e = std::getenv("CGTP_LOG");
+    return e ? std::atoi(e) : 0;
+  }();
+  return level;
+}
+
+void log_line(int level, const char* fmt, ...) {
+  if (log_level() < level) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "cgtp: %s\n", buf);
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -28,6 +50,7 @@ int fail(int code, const char* fmt, ...) {
   vsnprintf(buf, sizeof(buf), fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  log_line(1, "error %d: %s", code, buf);
   return code;
 }
 
@@ -439,13 +462,16 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   }
   for (const Irrep& r : P->in)
     if (r.l > kMaxL || r.mul <= 0) {
+      const Irrep bad = r;   // copied: r refers into the plan deleted below
       delete P;
-      return fail(CGTP_ERR_UNSUPPORTED, "input irrep %dx%d: need l <= %d and mul > 0", r.mul, r.l, kMaxL);
+      return fail(CGTP_ERR_UNSUPPORTED, "input irrep %dx%d: need l <= %d and mul > 0", bad.mul, bad.l, kMaxL);
     }
   for (const Irrep& r : P->sh)
     if (r.l > kMaxL || r.mul != 1) {
+      const Irrep bad = r;
       delete P;
-      return fail(CGTP_ERR_UNSUPPORTED, "edge SH irrep %dx%d: need l <= %d and multiplicity 1", r.mul, r.l, kMaxL);
+      return fail(CGTP_ERR_UNSUPPORTED, "edge SH irrep %dx%d: need l <= %d and multiplicity 1", bad.mul, bad.l,
+                  kMaxL);
     }
   std::vector<int> in_off;
   int64_t off = 0;
@@ -606,6 +632,9 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
       return fail(CGTP_ERR_HIP, "plan device set-up: %s", hipGetErrorString(e));
     }
   }
+  log_line(2, "plan %s x %s -> %s: %zu paths, %zu jobs, %zu groups, %zu launches on %d streams%s",
+           irreps_in, irreps_sh, P->irreps_out.c_str(), P->paths.size(), P->jobs.size(), P->groups.size(),
+           P->launches.size(), P->n_aux + 1, P->host_only ? " (host only)" : "");
   *out = P;
   return ok();
 }
@@ -700,15 +729,18 @@ int cgtp_neighbors_build(const float* pos, int64_t n_nodes, const float box[3], 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const NbrWorkspace w = carve_nbr_workspace(workspace, n_nodes, g);
   CGTP_HIP(launch_nbr_count(pos, int(n_nodes), g, w, row_ptr, s));
-  int32_t e_host = 0;
-  CGTP_HIP(hipMemcpyAsync(&e_host, row_ptr + n_nodes, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-  CGTP_HIP(hipStreamSynchronize(s));
+  int32_t stats[2] = {0, 0};   // edges, longest row
+  if (n_nodes > 0) {
+    CGTP_HIP(hipMemcpyAsync(stats, w.stats, sizeof(stats), hipMemcpyDeviceToHost, s));
+    CGTP_HIP(hipStreamSynchronize(s));
+  }
+  const int32_t e_host = stats[0];
   *n_edges = e_host;
   if (e_host > edge_capacity)
     return fail(CGTP_ERR_CAPACITY, "edge list needs %d entries, capacity is %lld", e_host, (long long)edge_capacity);
   if (e_host > 0) {
     if (!col || !shift) return fail(CGTP_ERR_INVALID_ARG, "col/shift NULL with edges present");
-    CGTP_HIP(launch_nbr_fill(pos, int(n_nodes), g, w, row_ptr, col, shift, s));
+    CGTP_HIP(launch_nbr_fill(pos, int(n_nodes), g, w, row_ptr, col, shift, stats[1], s));
   }
   return ok();
 }

@@ -8,6 +8,7 @@
 #include <cmath>
 
 #include "launch.hpp"
+#include "nbr.hpp"
 #include "sh_eval.hpp"
 #include "variants.hpp"
 
@@ -50,17 +51,30 @@ __device__ inline int block_exclusive_scan(int v, int* wsum, int& total) {
   return excl;
 }
 
-// out[k] = sum_{q<k} in[q] for k <= n (out has n+1 entries).  One workgroup.
-__global__ void __launch_bounds__(kScanThreads) scan_exclusive_kernel(const int32_t* in, int32_t* out, int n) {
+// out[k] = sum_{q<k} in[q] for k <= n (out has n+1 entries).  One workgroup.  stats
+// (may be null) receives {sum, largest value}.
+__global__ void __launch_bounds__(kScanThreads) scan_exclusive_kernel(const int32_t* in, int32_t* out, int n,
+                                                                     int32_t* stats) {
   __shared__ int wsum[kScanWaves + 1];
-  int carry = 0;
+  __shared__ int s_max;
+  if (threadIdx.x == 0) s_max = 0;
+  int carry = 0, vmax = 0;
   for (int base = 0; base < n; base += kScanThreads) {
     const int idx = base + threadIdx.x;
     const int v = idx < n ? in[idx] : 0;
+    vmax = max(vmax, v);
     int total;
     const int ex = block_exclusive_scan(v, wsum, total);
     if (idx < n) out[idx] = carry + ex;
     carry += total;
+  }
+  if (stats) {
+    atomicMax(&s_max, vmax);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      stats[0] = carry;
+      stats[1] = s_max;
+    }
   }
   if (threadIdx.x == 0) out[n] = carry;
 }
@@ -151,6 +165,139 @@ __device__ inline void for_each_stencil_cell(int c, const GridArgs& g, F&& f) {
   }
 }
 
+// Wave-per-atom passes: the 64 lanes of a wave take atom i's candidates (the atoms of its
+// distinct stencil cells, as one flattened list) 64 at a time, each testing one with the
+// same predicate.  The stencil's cells and the running totals of their atom counts sit
+// in a small per-wave LDS table that each lane searches for its candidate's cell.
+constexpr int kNbrWaves = 4;         // waves (atoms) per workgroup
+constexpr int kNbrRowCap = 1024;     // neighbours of one atom that the fill pass ranks in LDS
+
+struct StencilTable {
+  int pre[32];     // atoms in the stencil cells before cell s
+  int start[32];   // cell s's first entry in cell_atoms
+};
+
+// Fills this wave's table for cell c; returns the stencil's atom count (every lane).
+__device__ inline int stencil_table(int c, const GridArgs& g, const int32_t* __restrict__ cell_start,
+                                    StencilTable& t) {
+  const int lane = lane_id();
+  const int cx = c % g.nc[0], cy = (c / g.nc[0]) % g.nc[1], cz = c / (g.nc[0] * g.nc[1]);
+  int lo[3], cnt3[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    lo[k] = g.nc[k] >= 3 ? -1 : 0;
+    cnt3[k] = (g.nc[k] >= 2 ? 1 : 0) - lo[k] + 1;   // distinct offsets along k
+  }
+  const int n_cells = cnt3[0] * cnt3[1] * cnt3[2];
+  int cnt = 0, beg = 0;
+  if (lane < n_cells) {
+    const int ix = lane % cnt3[0], iy = (lane / cnt3[0]) % cnt3[1], iz = lane / (cnt3[0] * cnt3[1]);
+    const int x = (cx + lo[0] + ix + g.nc[0]) % g.nc[0];
+    const int y = (cy + lo[1] + iy + g.nc[1]) % g.nc[1];
+    const int z = (cz + lo[2] + iz + g.nc[2]) % g.nc[2];
+    const int cell = (z * g.nc[1] + y) * g.nc[0] + x;
+    beg = cell_start[cell];
+    cnt = cell_start[cell + 1] - beg;
+  }
+  int inc = cnt;
+#pragma unroll
+  for (int d = 1; d < 32; d <<= 1) {
+    const int u = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += u;
+  }
+  if (lane < 32) {
+    t.pre[lane] = inc - cnt;
+    t.start[lane] = beg;
+  }
+  return __shfl(inc, 31, kWave);
+}
+
+// Candidate q of the stencil (0 <= q < total): its atom id.
+__device__ inline int stencil_atom(int q, const StencilTable& t, const int32_t* __restrict__ cell_atoms) {
+  int s = 0;   // the last cell whose running total is at most q (binary search over 32)
+#pragma unroll
+  for (int b = 16; b > 0; b >>= 1)
+    if (t.pre[s + b] <= q) s += b;
+  return cell_atoms[t.start[s] + (q - t.pre[s])];
+}
+
+__global__ void __launch_bounds__(kNbrWaves * kWave) nbr_count_wave_kernel(
+    const float* __restrict__ pos, int n, GridArgs g, const int32_t* __restrict__ atom_cell,
+    const int32_t* __restrict__ cell_start, const int32_t* __restrict__ cell_atoms, int32_t* __restrict__ row_count) {
+  __shared__ StencilTable tab[kNbrWaves];
+  const int wave = threadIdx.x / kWave;
+  const int i = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kNbrWaves + wave);
+  if (i >= n) return;   // no barrier in this kernel: a wave may leave alone
+  StencilTable& t = tab[wave];
+  const int total = stencil_table(atom_cell[i], g, cell_start, t);
+  __builtin_amdgcn_wave_barrier();
+  int cnt = 0;
+  for (int q0 = 0; q0 < total; q0 += kWave) {
+    const int q = q0 + lane_id();
+    bool hit = false;
+    if (q < total) {
+      const int j = stencil_atom(q, t, cell_atoms);
+      int8_t sh[3];
+      hit = j != i && pair_within(pos, i, j, g, sh);
+    }
+    cnt += __popcll(__ballot(hit));
+  }
+  if (lane_id() == 0) row_count[i] = cnt;
+}
+
+// Fill of rows of at most kNbrRowCap neighbours: the wave compacts atom i's neighbours
+// into LDS (in candidate order, ballot-ranked) and writes each at its rank among them by
+// sender id, so the row comes out sorted by j (the ids of one row are distinct).
+__global__ void __launch_bounds__(kNbrWaves * kWave) nbr_fill_wave_kernel(
+    const float* __restrict__ pos, int n, GridArgs g, const int32_t* __restrict__ atom_cell,
+    const int32_t* __restrict__ cell_start, const int32_t* __restrict__ cell_atoms,
+    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col, int8_t* __restrict__ shift) {
+  __shared__ StencilTable tab[kNbrWaves];
+  __shared__ int s_j[kNbrWaves][kNbrRowCap];
+  __shared__ int s_code[kNbrWaves][kNbrRowCap];   // (s0 + 1) 9 + (s1 + 1) 3 + (s2 + 1)
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int i = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * kNbrWaves + wave);
+  if (i >= n) return;
+  const int rb = row_ptr[i], deg = row_ptr[i + 1] - rb;
+  if (deg > kNbrRowCap || deg == 0) return;   // long rows: nbr_fill_kernel
+  StencilTable& t = tab[wave];
+  const int total = stencil_table(atom_cell[i], g, cell_start, t);
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int m = 0;
+  for (int q0 = 0; q0 < total; q0 += kWave) {
+    const int q = q0 + lane;
+    bool hit = false;
+    int j = 0;
+    int8_t sh[3] = {0, 0, 0};
+    if (q < total) {
+      j = stencil_atom(q, t, cell_atoms);
+      hit = j != i && pair_within(pos, i, j, g, sh);
+    }
+    const unsigned long long bal = __ballot(hit);
+    const int at = m + __popcll(bal & lt);
+    if (hit && at < deg) {   // at < deg always: the count pass used the same predicate
+      s_j[wave][at] = j;
+      s_code[wave][at] = (sh[0] + 1) * 9 + (sh[1] + 1) * 3 + (sh[2] + 1);
+    }
+    m += __popcll(bal);
+  }
+  m = min(m, deg);
+  __builtin_amdgcn_wave_barrier();
+  for (int k = lane; k < m; k += kWave) {
+    const int jk = s_j[wave][k];
+    int r = 0;
+    for (int u = 0; u < m; ++u) r += s_j[wave][u] < jk;
+    const int code = s_code[wave][k];
+    const int at = rb + r;
+    col[at] = jk;
+    shift[3 * at + 0] = int8_t(code / 9 - 1);
+    shift[3 * at + 1] = int8_t((code / 3) % 3 - 1);
+    shift[3 * at + 2] = int8_t(code % 3 - 1);
+  }
+}
+
 __global__ void nbr_count_kernel(const float* __restrict__ pos, int n, GridArgs g,
                                  const int32_t* __restrict__ atom_cell,
                                  const int32_t* __restrict__ cell_start,
@@ -177,6 +324,7 @@ __global__ void nbr_fill_kernel(const float* __restrict__ pos, int n, GridArgs g
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int beg = row_ptr[i];
+  if (row_ptr[i + 1] - beg <= kNbrRowCap) return;   // filled by nbr_fill_wave_kernel
   int end = beg;
   for_each_stencil_cell(atom_cell[i], g, [&](int c) {
     for (int k = cell_start[c]; k < cell_start[c + 1]; ++k) {
@@ -522,7 +670,7 @@ static size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t nbr_workspace_bytes(int64_t n, const NbrGrid& g) {
   const size_t nc = size_t(g.n_cells());
-  return align256(nc * 4) + align256((nc + 1) * 4) + 3 * align256(size_t(n) * 4 + 4);
+  return align256(nc * 4) + align256((nc + 1) * 4) + 3 * align256(size_t(n) * 4 + 4) + 256;
 }
 
 NbrWorkspace carve_nbr_workspace(void* ws, int64_t n, const NbrGrid& g) {
@@ -538,6 +686,8 @@ NbrWorkspace carve_nbr_workspace(void* ws, int64_t n, const NbrGrid& g) {
   w.cell_atoms = reinterpret_cast<int32_t*>(p);
   p += align256(size_t(n) * 4 + 4);
   w.row_count = reinterpret_cast<int32_t*>(p);
+  p += align256(size_t(n) * 4 + 4);
+  w.stats = reinterpret_cast<int32_t*>(p);
   return w;
 }
 
@@ -559,24 +709,28 @@ hipError_t launch_nbr_count(const float* pos, int n, const NbrGrid& g, const Nbr
   // cell_count doubles as the fill cursor: clear, count, scan, clear, bin
   fill_i32_kernel<<<ceil_div(nc, tb), tb, 0, s>>>(w.cell_count, nc, 0);
   if (n > 0) nbr_assign_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_count);
-  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.cell_count, w.cell_start, nc);
+  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.cell_count, w.cell_start, nc, nullptr);
   fill_i32_kernel<<<ceil_div(nc, tb), tb, 0, s>>>(w.cell_count, nc, 0);
   if (n > 0) {
     nbr_bin_kernel<<<ceil_div(n, tb), tb, 0, s>>>(n, w.atom_cell, w.cell_start, w.cell_count, w.cell_atoms);
-    nbr_count_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start, w.cell_atoms,
-                                                    w.row_count);
+    nbr_count_wave_kernel<<<ceil_div(n, kNbrWaves), kNbrWaves * kWave, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start,
+                                                                              w.cell_atoms, w.row_count);
   }
-  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.row_count, row_ptr, n);
+  scan_exclusive_kernel<<<1, kScanThreads, 0, s>>>(w.row_count, row_ptr, n, w.stats);
   return hipGetLastError();
 }
 
 hipError_t launch_nbr_fill(const float* pos, int n, const NbrGrid& g, const NbrWorkspace& w,
-                           const int32_t* row_ptr, int32_t* col, int8_t* shift, hipStream_t s) {
+                           const int32_t* row_ptr, int32_t* col, int8_t* shift, int max_degree, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const GridArgs a = to_args(g);
-  const int tb = 256;
-  nbr_fill_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start, w.cell_atoms, row_ptr,
-                                                 col, shift);
+  nbr_fill_wave_kernel<<<ceil_div(n, kNbrWaves), kNbrWaves * kWave, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start,
+                                                                           w.cell_atoms, row_ptr, col, shift);
+  if (max_degree > kNbrRowCap) {   // rows too long for the wave's LDS list: one thread each
+    const int tb = 256;
+    nbr_fill_kernel<<<ceil_div(n, tb), tb, 0, s>>>(pos, n, a, w.atom_cell, w.cell_start, w.cell_atoms, row_ptr,
+                                                   col, shift);
+  }
   return hipGetLastError();
 }
 

@@ -92,6 +92,24 @@ def test_neighbors_small_boxes(dev, n, box_len, cutoff, seed):
     assert np.array_equal(g_sh.cpu().numpy(), sh)
 
 
+def test_neighbors_long_rows(dev):
+    # a dense box with a denser cluster: rows of about 800 to 1400 neighbours, so that
+    # some rows are longer than the wave-per-atom fill ranks in LDS (1024) and take the
+    # one-thread-per-atom path, and the rest do not
+    rng = np.random.default_rng(17)
+    box_len, cutoff = 12.0, 5.5
+    pos = np.concatenate([rng.random((2000, 3)) * box_len, 4.0 + rng.random((500, 3)) * 3.0]).astype(np.float32)
+    pos[pos >= np.float32(box_len)] = 0
+    box = np.full(3, box_len, dtype=np.float32)
+    rp, col, sh = O.neighbors(pos, box, cutoff)
+    deg = np.diff(rp)
+    assert deg.max() > 1024 and deg.min() <= 1024
+    g_rp, g_col, g_sh = C.neighbors_build(_t(pos, dev), box, cutoff)
+    assert np.array_equal(g_rp.cpu().numpy(), rp)
+    assert np.array_equal(g_col.cpu().numpy(), col)
+    assert np.array_equal(g_sh.cpu().numpy(), sh)
+
+
 def test_neighbors_empty(dev):
     pos = torch.zeros((0, 3), dtype=torch.float32, device=dev)
     rp, col, sh = C.neighbors_build(pos, [5.0, 5.0, 5.0], 2.0)
