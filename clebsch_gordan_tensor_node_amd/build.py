@@ -3,8 +3,7 @@
     python -m clebsch_gordan_tensor_node_amd.build [--incremental] [-j N]
 
 Every translation unit is compiled in parallel; the convolution kernel source is
-compiled once per kernel class (-DCGTP_CONV_CLASS=k), the backward's twice (its edge
-pass and its other passes, -DCGTP_BWD_PART=0/1).  Objects go to ``_build/`` at the
+compiled once per kernel class (-DCGTP_CONV_CLASS=k).  Objects go to ``_build/`` at the
 repository root; the shared library is written next to this file.
 """
 from __future__ import annotations
@@ -42,9 +41,8 @@ def _hipcc() -> str:
 
 
 def _units():
-    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o")]
-    for part in range(2):   # the backward's edge pass, and its other passes
-        units.append(("kernels_bwd.hip", [f"-DCGTP_BWD_PART={part}"], f"kernels_bwd_p{part}.o"))
+    units = [("cgtp_api.hip", [], "cgtp_api.o"), ("kernels_graph.hip", [], "kernels_graph.o"),
+             ("kernels_bwd.hip", [], "kernels_bwd.o")]
     for c in range(N_CONV_CLASSES):
         units.append(("kernels_conv.hip", [f"-DCGTP_CONV_CLASS={c}"], f"kernels_conv_c{c}.o"))
     return units
@@ -91,8 +89,8 @@ def build(incremental: bool = False, jobs: int | None = None, verbose: bool = Tr
 
     t0 = time.time()
     # the slowest units (the backward's edge pass, the l >= 4 conv classes) start first
-    slow = {"kernels_bwd_p0.o": 0, "kernels_conv_c6.o": 1, "kernels_conv_c7.o": 2, "kernels_conv_c8.o": 3,
-            "kernels_conv_c1.o": 4, "kernels_bwd_p1.o": 5, "kernels_conv_c5.o": 6}
+    slow = {"kernels_conv_c6.o": 0, "kernels_conv_c7.o": 1, "kernels_conv_c8.o": 2, "kernels_conv_c1.o": 3,
+            "kernels_conv_c5.o": 4, "kernels_bwd.o": 5, "kernels_conv_c4.o": 6}
     order = sorted(range(len(_units())), key=lambda k: slow.get(_units()[k][2], 99))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         done = dict(zip(order, ex.map(compile_one, [_units()[k] for k in order])))

@@ -190,6 +190,13 @@ struct cgtp_plan_s {
   int lmax = 0;                      // largest l of the plan
   PathDev* d_paths = nullptr;
   int32_t* d_irrep = nullptr;
+  // the backward edge pass's dL/dY partials: per job (a path and channel block) a block
+  // of 2 l2 + 1 values in a row of gy_stride (job order), and the {l2, offset} list of the
+  // blocks that the force pass adds
+  std::vector<int32_t> job_gy;
+  std::vector<int2> gy_list;
+  int32_t* d_job_gy = nullptr;
+  int2* d_gy_list = nullptr;
   // Forward launches: a kernel class and a range of its groups each.  Launches write
   // disjoint output columns and only read the inputs, so the plan spreads them over the
   // caller's stream (stream 0) and up to kAuxStreams streams of its own (stream k = aux
@@ -567,6 +574,13 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     P->lmax = std::max(P->lmax, std::max(p.l1, std::max(p.l2, p.l3)));
     P->pdev.push_back(d);
   }
+  P->gy_stride = 0;
+  for (const Job& j : P->jobs) {
+    const int l2 = variant_desc(j.variant).l2;
+    P->job_gy.push_back(P->gy_stride);
+    P->gy_list.push_back(make_int2(l2, P->gy_stride));
+    P->gy_stride += 2 * l2 + 1;
+  }
   {
     const int ni = int(P->in.size());
     std::vector<int32_t> start(ni + 1, 0), list;
@@ -607,17 +621,25 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     P->device = dev;
     const size_t jb = align256(P->jobs.size() * sizeof(Job));
     const size_t pb = align256(P->pdev.size() * sizeof(PathDev));
-    const size_t ib = P->irrep_tab.size() * sizeof(int32_t);
-    hipError_t e = hipMalloc(&P->d_tables, jb + pb + ib);
+    const size_t ib = align256(P->irrep_tab.size() * sizeof(int32_t));
+    const size_t gb = align256(P->job_gy.size() * sizeof(int32_t));
+    const size_t lb = P->gy_list.size() * sizeof(int2);
+    hipError_t e = hipMalloc(&P->d_tables, jb + pb + ib + gb + lb);
     if (e == hipSuccess) {
       char* base = static_cast<char*>(P->d_tables);
       P->d_jobs = reinterpret_cast<Job*>(base);
       P->d_paths = reinterpret_cast<PathDev*>(base + jb);
       P->d_irrep = reinterpret_cast<int32_t*>(base + jb + pb);
+      P->d_job_gy = reinterpret_cast<int32_t*>(base + jb + pb + ib);
+      P->d_gy_list = reinterpret_cast<int2*>(base + jb + pb + ib + gb);
       e = hipMemcpy(P->d_jobs, P->jobs.data(), P->jobs.size() * sizeof(Job), hipMemcpyHostToDevice);
       if (e == hipSuccess)
         e = hipMemcpy(P->d_paths, P->pdev.data(), P->pdev.size() * sizeof(PathDev), hipMemcpyHostToDevice);
-      if (e == hipSuccess) e = hipMemcpy(P->d_irrep, P->irrep_tab.data(), ib, hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(P->d_irrep, P->irrep_tab.data(), P->irrep_tab.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(P->d_job_gy, P->job_gy.data(), P->job_gy.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+      if (e == hipSuccess) e = hipMemcpy(P->d_gy_list, P->gy_list.data(), lb, hipMemcpyHostToDevice);
     }
     // auxiliary streams (default priority, not synchronising with the null stream) and
     // the fork/join events of the concurrent launches
@@ -808,6 +830,41 @@ int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float c
 
 }  // extern "C"
 
+// The workgroup layout of one launch of the fused conv kernel (its groups and blocks) in
+// a; returns its workgroup count.  Workgroups are dispatched block by block: a block of
+// B = 64 / 2^lg_min receivers (the largest node group of the launch) holds B / S_g node
+// groups of every group g, so the groups of one block, which read the same weight rows,
+// run at the same time.
+template <typename T>
+static int64_t fill_launch(const cgtp_plan_s& P, const cgtp_plan_s::ConvLaunch& L, int64_t n_nodes, ConvArgsT<T>& a) {
+  a.n_groups = L.g1 - L.g0;
+  for (int k = 0; k < kMaxGroupsPerLaunch; ++k) a.g_start[k] = kMaxInt32;   // past the groups
+  int lg_min = 6;
+  for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, P.groups[k].lanes_log2);
+  int per_block = 0;
+  for (int k = L.g0; k < L.g1; ++k) {
+    const Group& G = P.groups[k];
+    a.g_start[k - L.g0] = per_block;
+    GroupArgs& ga = a.grp[k - L.g0];
+    ga.start = per_block;
+    ga.first_job = G.first_job;
+    ga.n_jobs = G.n_jobs;
+    ga.lanes_log2 = G.lanes_log2;
+    ga.y0 = G.y0;
+    ga.y4 = G.y4;
+    per_block += 1 << (G.lanes_log2 - lg_min);
+  }
+  const int64_t block = 64 >> lg_min;
+  const int64_t nblocks = (n_nodes + block - 1) / block;
+  // whole rounds of kXcds blocks: blocks past the last are empty workgroups
+  const int64_t wgs = (nblocks + kXcds - 1) / kXcds * kXcds * per_block;
+  a.blk_wgs = per_block;
+  a.blk_lg_min = lg_min;
+  a.n_blocks = int(nblocks);
+  a.total_wgs = int(std::min<int64_t>(wgs, kMaxInt32));
+  return wgs;
+}
+
 // The forward in element type T (float, or double for plans made with CGTP_PLAN_FP64).
 template <typename T>
 static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const T cell[9],
@@ -881,37 +938,7 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
   a.sh_stride = P->sh_pad;
-  // Workgroups are dispatched block by block: a block of B = 64 / 2^lg_min receivers
-  // (the largest node group of the launch) holds B / S_g node groups of every group g, so
-  // the groups of one block, which read the same weight rows, run at the same time.
-  auto fill = [&](const cgtp_plan_s::ConvLaunch& L) -> int64_t {
-    a.n_groups = L.g1 - L.g0;
-    for (int k = 0; k < kMaxGroupsPerLaunch; ++k) a.g_start[k] = kMaxInt32;   // past the groups
-    int lg_min = 6;
-    for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, P->groups[k].lanes_log2);
-    int per_block = 0;
-    for (int k = L.g0; k < L.g1; ++k) {
-      const Group& G = P->groups[k];
-      a.g_start[k - L.g0] = per_block;
-      GroupArgs& ga = a.grp[k - L.g0];
-      ga.start = per_block;
-      ga.first_job = G.first_job;
-      ga.n_jobs = G.n_jobs;
-      ga.lanes_log2 = G.lanes_log2;
-      ga.y0 = G.y0;
-      ga.y4 = G.y4;
-      per_block += 1 << (G.lanes_log2 - lg_min);
-    }
-    const int64_t block = 64 >> lg_min;
-    const int64_t nblocks = (n_nodes + block - 1) / block;
-    // whole rounds of kXcds blocks: blocks past the last are empty workgroups
-    const int64_t wgs = (nblocks + kXcds - 1) / kXcds * kXcds * per_block;
-    a.blk_wgs = per_block;
-    a.blk_lg_min = lg_min;
-    a.n_blocks = int(nblocks);
-    a.total_wgs = int(std::min<int64_t>(wgs, kMaxInt32));
-    return wgs;
-  };
+  auto fill = [&](const cgtp_plan_s::ConvLaunch& L) -> int64_t { return fill_launch(*P, L, n_nodes, a); };
   const auto& launches = P->launches;
   for (const auto& L : launches)
     if (fill(L) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
@@ -1029,6 +1056,7 @@ struct BwdWorkspace {
   FwdWorkspace fwd;
   int32_t *t_cnt, *t_row_ptr, *t_slot, *t_recv;
   float *gyp, *grad_r, *xp;
+  float* scratch_row;   // the edge pass's stores of lanes with nothing to store
   size_t bytes;
 };
 
@@ -1049,6 +1077,7 @@ static BwdWorkspace carve_bwd(const cgtp_plan_s& P, int64_t n, int64_t e, void* 
   w.gyp = reinterpret_cast<float*>(take(size_t(e) * size_t(P.gy_stride) * 4));
   w.grad_r = reinterpret_cast<float*>(take(size_t(e) * 12));
   w.xp = reinterpret_cast<float*>(take(size_t(n) * size_t(P.xp_stride) * 4));
+  w.scratch_row = reinterpret_cast<float*>(take(64 * 4));
   w.bytes = off;
   return w;
 }
@@ -1075,9 +1104,12 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   const bool any = grad_x || grad_w || grad_pos;
   if (n_nodes > 0 && any && (!grad_out || !x || !pos)) return fail(CGTP_ERR_INVALID_ARG, "NULL node array");
   if (n_edges > 0 && any && (!col || !w)) return fail(CGTP_ERR_INVALID_ARG, "NULL edge array");
-  if (!aligned(x, 4) || !aligned(w, 4) || !aligned(pos, 4) || !aligned(col, 4) || !aligned(gate, 4) ||
-      !aligned(grad_out, 4) || !aligned(grad_x, 4) || !aligned(grad_w, 4) || !aligned(grad_pos, 4))
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(grad_out, 16) || !aligned(grad_w, 16))
+    return fail(CGTP_ERR_INVALID_ARG, "x, w, grad_out and grad_w must be 16-byte aligned");
+  if (!aligned(pos, 4) || !aligned(col, 4) || !aligned(gate, 4) || !aligned(grad_x, 4) || !aligned(grad_pos, 4))
     return fail(CGTP_ERR_INVALID_ARG, "misaligned pointer");
+  if (double(n_nodes) * double(P->f_in) * 4.0 >= 4294967296.0)
+    return fail(CGTP_ERR_UNSUPPORTED, "x is 4 GiB or larger (32-bit byte offsets)");
   const BwdWorkspace ws = carve_bwd(*P, n_nodes, n_edges, workspace);
   if (!workspace || ws_bytes < ws.bytes)
     return fail(CGTP_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, ws.bytes);
@@ -1100,7 +1132,13 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   g.n_nodes = int(n_nodes);
   g.n_edges = int(n_edges);
   fill_cell(g, cell);
-  CGTP_HIP(launch_rows(g, P->l_sh_max, s));
+  // and the node order by active degree that the edge pass walks, as in the forward
+  if (!mask && !gate) {
+    CGTP_HIP(launch_rows_order(g, P->l_sh_max, ws.fwd.node_info, s));
+  } else {
+    CGTP_HIP(launch_rows(g, P->l_sh_max, s));
+    CGTP_HIP(launch_degree_order(ws.fwd.deg, int(n_nodes), row_ptr, ws.fwd.node_info, s));
+  }
   BwdArgs a{};
   a.x = x;
   a.w = w;
@@ -1127,6 +1165,8 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   a.grad_x = grad_x;
   a.grad_w = grad_w;
   a.gyp = ws.gyp;
+  a.gy_list = P->d_gy_list;
+  a.n_gy = int(P->gy_list.size());
   a.grad_r = ws.grad_r;
   a.xp = ws.xp;
   a.xp_stride = P->xp_stride;
@@ -1143,8 +1183,35 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
   a.want_gy = grad_pos != nullptr;
   a.has_cell = cell != nullptr;
   for (int k = 0; k < 9; ++k) a.cell[k] = cell ? double(cell[k]) : 0.0;
-  // 2. w-gradient and the per-path dL/dY partials (receiver-major)
-  if (grad_w || grad_pos) CGTP_HIP(launch_bwd_edges(a, P->lmax > 3, s));
+  // 2. the edge pass: the fused conv kernel's workgroups in their backward mode write the
+  //    w-gradient of every active edge and the per-job dL/dY partials of every active
+  //    slot; the rows of inactive edges are zeroed apart
+  if (grad_w) CGTP_HIP(launch_zero_inactive(row_ptr, mask, gate, int(n_nodes), grad_w, int(P->w), s));
+  if (grad_w || grad_pos) {
+    ConvArgsT<float> c{};
+    c.x = x;
+    c.w = w;
+    c.sh = static_cast<const float*>(ws.fwd.sh);
+    c.node_info = ws.fwd.node_info;
+    c.act_e = ws.fwd.act_e;
+    c.act_j = ws.fwd.act_j;
+    c.jobs = P->d_jobs;
+    c.n_nodes = int(n_nodes);
+    c.f_in = int(P->f_in);
+    c.f_out = int(P->f_out);
+    c.w_stride = int(P->w);
+    c.sh_stride = P->sh_pad;
+    c.grad_out = grad_out;
+    c.grad_w = grad_w;
+    c.gyp = grad_pos ? ws.gyp : nullptr;
+    c.job_gy = P->d_job_gy;
+    c.scratch_row = ws.scratch_row;
+    c.gy_stride = P->gy_stride;
+    for (const auto& L : P->launches) {
+      if (fill_launch(*P, L, n_nodes, c) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
+      CGTP_HIP(launch_conv_bwd(c, L.cls, s));
+    }
+  }
   // 3. active slots grouped by sender, then the x-gradient and the forces
   if (grad_x || grad_pos) CGTP_HIP(launch_bwd_transpose(a, ws.t_cnt, ws.t_row_ptr, ws.t_slot, ws.t_recv, s));
   if (grad_x) CGTP_HIP(launch_bwd_x(a, P->lmax > 3, s));

@@ -71,6 +71,15 @@ struct ConvArgsT {
   const int32_t* act_j;       // their senders
   T* out;
   const Job* jobs;            // the plan's job table
+  // backward edge pass only (else null): dL/d out, dL/dw, the per-job dL/dY partials
+  // [slot, gy_stride] with job j's block at job_gy[j], and a scratch row for lanes with
+  // nothing to store
+  const T* grad_out;
+  T* grad_w;
+  T* gyp;
+  const int32_t* job_gy;
+  T* scratch_row;
+  int32_t gy_stride;
   int32_t n_nodes;
   int32_t f_in;
   int32_t f_out;
@@ -129,13 +138,14 @@ struct BwdArgs {
   const int32_t* t_recv;
   float* grad_x;
   float* grad_w;
-  float* gyp;                 // [slot, gy_stride] per-path dL/dY partials
+  float* gyp;                 // [slot, gy_stride] per-job dL/dY partials
+  const int2* gy_list;        // per job: {l2, offset of its block in a row of gyp}
   float* xp;                  // [node, xp_stride] per-path x-gradient partials
   float* grad_r;              // [slot, 3] dL/dr
   float* grad_pos;
   int32_t n_nodes, n_paths, n_irreps;
   int32_t f_in, f_out, w_stride, sh_stride, gy_stride, l_sh_max;
-  int32_t want_gy, has_cell, xp_stride;
+  int32_t want_gy, has_cell, xp_stride, n_gy;
   double cell[9];
 };
 

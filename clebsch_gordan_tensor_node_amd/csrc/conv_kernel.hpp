@@ -214,6 +214,7 @@ struct ConvSmem {
   uint32_t sx[(1 << kStageLog2) + kWave];   // j f_in (x element offset of the sender's row)
   uint32_t sw[(1 << kStageLog2) + kWave];   // (e - row start) W (w offset from the receiver's rows)
   uint32_t sy[(1 << kStageLog2) + kWave];   // q sh_stride (SH offset from the receiver's rows)
+  uint32_t sg[(1 << kStageLog2) + kWave];   // q gy_stride (backward: dL/dY row offset)
   int4 slot[kWave];                 // receiver records {node or -1, row start, active degree, 0}
 };
 
@@ -236,6 +237,54 @@ __device__ __forceinline__ const T* byte_off(const T* base, uint32_t bytes) {
   return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + bytes);
 }
 
+// The backward of one edge for K channels (the lane's share), with g the receiver's
+// output gradient [K][N3], x the sender's features [K][N1] (scaled by w on return), w the
+// edge's weights and Y its harmonics:
+//   gw[k]    = sum_m3 g[k][m3] sum_m1 A[m1][m3] x[k][m1]          (dL/dw, A = C . Y)
+//   gy[m2]   = sum_k w[k] sum_{m1,m3} C[m1,m2,m3] x[k][m1] g[k][m3] (this lane's part of dL/dY)
+template <typename T, int L1, int L2, int L3, int K>
+__device__ __forceinline__ void backward_edge(const T* g, T* x, const T* w, const T* Y, T* gw, T* gy) {
+  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
+#pragma unroll
+  for (int k = 0; k < K; ++k) gw[k] = T(0);
+  static_for<0, N3>([&](auto M3c) {
+    constexpr int M3 = decltype(M3c)::value;
+    T tk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) tk[k] = T(0);
+    static_for<0, N1>([&](auto M1c) {
+      constexpr int M1 = decltype(M1c)::value;
+      if constexpr (kCG<L1, L2, L3>.a_nonzero(M1, M3)) {
+        const T A = a_entry<T, L1, L2, L3, M1, M3>(Y);
+#pragma unroll
+        for (int k = 0; k < K; ++k) tk[k] = fma_t(A, x[k * N1 + M1], tk[k]);
+      }
+    });
+#pragma unroll
+    for (int k = 0; k < K; ++k) gw[k] = fma_t(g[k * N3 + M3], tk[k], gw[k]);
+  });
+#pragma unroll
+  for (int q = 0; q < K * N1; ++q) x[q] *= w[q / N1];
+#pragma unroll
+  for (int m = 0; m < N2; ++m) gy[m] = T(0);
+  static_for<0, N1>([&](auto M1c) {
+    constexpr int M1 = decltype(M1c)::value;
+    static_for<0, N3>([&](auto M3c) {
+      constexpr int M3 = decltype(M3c)::value;
+      if constexpr (kCG<L1, L2, L3>.a_nonzero(M1, M3)) {
+        T pq = T(0);   // sum over the lane's channels of w x[m1] g[m3]
+#pragma unroll
+        for (int k = 0; k < K; ++k) pq = fma_t(x[k * N1 + M1], g[k * N3 + M3], pq);
+        static_for<0, N2>([&](auto M2c) {
+          constexpr int M2 = decltype(M2c)::value;
+          constexpr T c = kCG<L1, L2, L3>.template coef<T>(M1, M2, M3);
+          if constexpr (c != T(0)) gy[M2] = fma_t(c, pq, gy[M2]);
+        });
+      }
+    });
+  });
+}
+
 // One wave of a workgroup.  Waves 0 .. kConvJobs-1 are consumers, one job each (or idle
 // when the group has fewer jobs); wave kConvJobs is the producer.  Consumer lane layout:
 // lane = (receiver slot ns, channel lane t) with T = 2^lg channel lanes and S = 64 / T
@@ -249,8 +298,8 @@ __device__ __forceinline__ const T* byte_off(const T* base, uint32_t bytes) {
 // receiver without active edges stores zeros.  Every load of a pipeline step is issued
 // unconditionally: a skipped load would make the wave's in-order memory counter
 // ambiguous and force full waits.
-template <int C, typename T, int L1, int L2, int L3, int K>
-__device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int ng, int lg, int y0, int y4,
+template <int C, typename T, bool BWD, int L1, int L2, int L3, int K>
+__device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int job, int ng, int lg, int y0, int y4,
                                         int wave, bool has_job, ConvSmem<C, T>& sm) {
   constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
   constexpr int V = kVec<T>;
@@ -293,6 +342,7 @@ __device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int
         sm.sx[at] = ox;
         sm.sw[at] = ow;
         sm.sy[at] = oy;
+        if constexpr (BWD) sm.sg[at] = oy / uint32_t(a.sh_stride) * uint32_t(a.gy_stride);
       }
     }
   };
@@ -391,6 +441,93 @@ __device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int
     return;
   }
 
+  if constexpr (BWD) {
+    // ---------------- consumer (backward): dL/dw and this job's dL/dY per edge ----------
+    // As the forward's consumer, but per edge step it writes the edge's w-gradient for
+    // its K channels and, summed over the receiver's lanes by a fixed butterfly, the
+    // job's dL/dY of the edge's slot.  Steps past a receiver's last edge repeat that edge
+    // (its weights are kept), so they store the same values again; lanes without edges or
+    // channels store into a scratch row.
+    constexpr int D = consumer_depth<T, K>();
+    const int t = lane & ((1 << lg) - 1);
+    const int ns = lane >> lg;
+    const int ch0 = t * K;
+    const int4 my = sm.slot[ns];
+    const bool mine = my.z > 0 && ch0 < n_ch;
+    const int w_sl = ns * srow;
+    const long rowoff = (long)(my.z > 0 ? my.y : 0) * a.w_stride + J.w_off + (ch0 < n_ch ? ch0 : 0);
+    const T* __restrict__ wbase = a.w + rowoff;
+    T* gwbase = a.grad_w ? a.grad_w + rowoff : nullptr;
+    T* gybase = a.gyp ? a.gyp + (long)(my.z > 0 ? my.y : 0) * a.gy_stride + a.job_gy[job] : nullptr;
+    const int x_rd = (ns * n_ch + ch0) * N1;
+    const int y_rd = ns * V * y4 + J.sh_off - y0;
+    T g[K * N3];
+    if (ch0 < n_ch && my.x >= 0) {
+      load_run<T, K, K * N3>(a.grad_out + (long)my.x * a.f_out + J.out_off + ch0 * N3, g);
+    } else {
+#pragma unroll
+      for (int q = 0; q < K * N3; ++q) g[q] = T(0);
+    }
+    T ring[D][K];
+    for (int qw = 0; qw < qmax; qw += (1 << cap_log2)) {
+      const int steps = min(1 << cap_log2, qmax - qw);
+      stage(qw, steps);
+      __syncthreads();
+      auto fetch = [&](int k) { return sm.sw[w_sl + min(k, steps - 1)] * B; };
+      auto issue = [&](uint32_t ow, T* b) {
+        load_k_stream<T, K>(byte_off(wbase, ow), b);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto use = [&](int k, T* b) {
+        __syncthreads();   // the producer has published step k
+#pragma unroll
+        for (int m = 0; m < K; ++m) asm volatile("" : "+v"(b[m]));
+        T wv[K];
+#pragma unroll
+        for (int m = 0; m < K; ++m) wv[m] = mine ? b[m] : T(0);
+        T xv[K * N1];
+        load_run<T, K, K * N1>(sm.x[k & 1] + x_rd, xv);
+        T Y[N2];
+        const T* ys = sm.y[k & 1] + y_rd;
+#pragma unroll
+        for (int m = 0; m < N2; ++m) Y[m] = ys[m];
+        T gw[K], gy[N2];
+        backward_edge<T, L1, L2, L3, K>(g, xv, wv, Y, gw, gy);
+        if (a.grad_w) {   // uniform: the w-gradient is requested
+          T* dst = mine ? reinterpret_cast<T*>(reinterpret_cast<char*>(gwbase) + sm.sw[w_sl + k] * B) : a.scratch_row;
+          store_run<T, K, K>(dst, gw);
+        }
+        if (a.gyp) {      // uniform: dL/dY is requested (for the position gradient)
+#pragma unroll
+          for (int m = 0; m < N2; ++m)
+#pragma unroll
+            for (int o = 1; o < (1 << 6); o <<= 1)
+              if (o < (1 << lg)) gy[m] += __shfl_xor(gy[m], o, kWave);
+          if (t == 0) {
+            T* gdst = my.z > 0 ? gybase + sm.sg[w_sl + k] : a.scratch_row;
+#pragma unroll
+            for (int m = 0; m < N2; ++m) gdst[m] = gy[m];
+          }
+        }
+      };
+      static_for<0, D - 1>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        issue(fetch(p), ring[p]);
+      });
+      uint32_t ow = fetch(D - 1);
+      for (int k0 = 0; k0 < steps; k0 += D) {
+        static_for<0, D>([&](auto Sx) {
+          constexpr int s = decltype(Sx)::value;
+          issue(ow, ring[(s + D - 1) % D]);
+          ow = fetch(k0 + s + D);
+          if (k0 + s < steps) use(k0 + s, ring[s]);
+        });
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
   // ---------------- consumer: this job's weights and accumulation ----------------
   constexpr int D = consumer_depth<T, K>();
   const int t = lane & ((1 << lg) - 1);
@@ -461,28 +598,30 @@ __device__ __forceinline__ void run_job(const ConvArgsT<T>& a, const Job& J, int
   }
 }
 
-template <int C, typename T, int LO, int HI>
-__device__ __forceinline__ void dispatch(int v, const ConvArgsT<T>& a, const Job& J, int ng, int lg, int y0, int y4,
-                                         int wave, bool has_job, ConvSmem<C, T>& sm) {
+template <int C, typename T, bool BWD, int LO, int HI>
+__device__ __forceinline__ void dispatch(int v, const ConvArgsT<T>& a, const Job& J, int job, int ng, int lg, int y0,
+                                         int y4, int wave, bool has_job, ConvSmem<C, T>& sm) {
   if constexpr (HI - LO == 1) {
-    if constexpr (class_contains(C, LO) && (sizeof(T) == 4 || variant_lmax(LO) <= kF64Lmax)) {
+    if constexpr (class_contains(C, LO) && (sizeof(T) == 4 || variant_lmax(LO) <= kF64Lmax) &&
+                  (!BWD || variant_lmax(LO) <= kBwdLmax)) {
       constexpr VariantDesc d = variant_desc(LO);
       constexpr int K = d.k == 1 ? 1 : kVec<T>;   // the vector form moves 16 bytes per lane
-      run_job<C, T, d.l1, d.l2, d.l3, K>(a, J, ng, lg, y0, y4, wave, has_job, sm);
+      run_job<C, T, BWD, d.l1, d.l2, d.l3, K>(a, J, job, ng, lg, y0, y4, wave, has_job, sm);
     }
   } else {
     constexpr int MID = (LO + HI) / 2;
     if (v < MID)
-      dispatch<C, T, LO, MID>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
+      dispatch<C, T, BWD, LO, MID>(v, a, J, job, ng, lg, y0, y4, wave, has_job, sm);
     else
-      dispatch<C, T, MID, HI>(v, a, J, ng, lg, y0, y4, wave, has_job, sm);
+      dispatch<C, T, BWD, MID, HI>(v, a, J, job, ng, lg, y0, y4, wave, has_job, sm);
   }
 }
 
 // One workgroup per (group, node group): the producer wave and one consumer wave per job
 // (consumer waves past the group's job count only keep the barrier count).  The producer
 // runs the first job's code path, which fixes l1, K and the channel block it gathers.
-template <int C, typename T>
+// BWD: the backward's edge pass (dL/dw and the per-job dL/dY) instead of the forward.
+template <int C, typename T, bool BWD>
 __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgsT<T> a) {
   // the hardware deals workgroups to the XCDs round-robin by index; the numbering puts
   // every workgroup of one receiver block on the same XCD, so that the block's groups
@@ -514,10 +653,11 @@ __global__ void __launch_bounds__(kConvThreads) conv_kernel(ConvArgsT<T> a) {
   const int tid = int(threadIdx.x);
   const int pos = ng * S + (tid & (S - 1));
   const int4 rec = a.node_info[min(pos, a.n_nodes - 1)];
-  const Job J = a.jobs[G.first_job + (has_job ? wave : 0)];
+  const int job = G.first_job + (has_job ? wave : 0);
+  const Job J = a.jobs[job];
   __shared__ ConvSmem<C, T> sm;
   sm.slot[tid & (S - 1)] = pos < a.n_nodes ? rec : make_int4(-1, 0, 0, 0);
-  dispatch<C, T, 0, kNumVariants>(J.variant, a, J, ng, lg, G.y0, G.y4, wave, has_job, sm);
+  dispatch<C, T, BWD, 0, kNumVariants>(J.variant, a, J, job, ng, lg, G.y0, G.y4, wave, has_job, sm);
 }
 
 }  // namespace
@@ -528,10 +668,18 @@ hipError_t launch_conv_class(const ConvArgsT<T>& args, hipStream_t s, hipEvent_t
   const int blocks = args.total_wgs;
   if (ev_start || ev_stop) {
     // the events are stamped by the dispatch itself: kernel time without launch gaps
-    hipExtLaunchKernelGGL(conv_kernel<C, T>, dim3(blocks), dim3(kConvThreads), 0, s, ev_start, ev_stop, 0, args);
+    hipExtLaunchKernelGGL(conv_kernel<C, T, false>, dim3(blocks), dim3(kConvThreads), 0, s, ev_start, ev_stop, 0,
+                          args);
   } else {
-    conv_kernel<C, T><<<blocks, kConvThreads, 0, s>>>(args);
+    conv_kernel<C, T, false><<<blocks, kConvThreads, 0, s>>>(args);
   }
+  return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_conv_bwd_class(const ConvArgsT<float>& args, hipStream_t s) {
+  if (args.total_wgs <= 0) return hipSuccess;
+  conv_kernel<C, float, true><<<args.total_wgs, kConvThreads, 0, s>>>(args);
   return hipGetLastError();
 }
 

@@ -644,6 +644,34 @@ __global__ void compact_kernel(const int32_t* __restrict__ row_ptr, const uint8_
   act_eid[act_row_ptr[lo] + rank] = e;
 }
 
+// One wave per row: the w-gradient rows of the row's inactive edges set to zero, the
+// lanes over the row's columns (16-byte stores when the rows allow).
+__global__ void __launch_bounds__(256) zero_inactive_kernel(const int32_t* __restrict__ row_ptr,
+                                                            const uint8_t* __restrict__ mask,
+                                                            const float* __restrict__ gate, int n_nodes,
+                                                            float* __restrict__ grad_w, int w_stride) {
+  const int row = __builtin_amdgcn_readfirstlane(int(blockIdx.x) * 4 + int(threadIdx.x) / kWave);
+  if (row >= n_nodes) return;
+  const int lane = lane_id();
+  const int rb = row_ptr[row], re = row_ptr[row + 1];
+  const bool vec = (w_stride % 4) == 0 && (reinterpret_cast<uintptr_t>(grad_w) % 16) == 0;
+  for (int b0 = rb; b0 < re; b0 += kWave) {
+    const int e = b0 + lane;
+    const bool off = e < re && ((mask && mask[e] == 0) || (gate && gate[e] == 0.0f));
+    unsigned long long bal = __ballot(off);
+    while (bal) {
+      const int k = __ffsll((long long)bal) - 1;
+      bal &= bal - 1;
+      float* r = grad_w + (long)(b0 + k) * w_stride;
+      if (vec) {
+        for (int c = lane; c < w_stride / 4; c += kWave) reinterpret_cast<float4*>(r)[c] = make_float4(0, 0, 0, 0);
+      } else {
+        for (int c = lane; c < w_stride; c += kWave) r[c] = 0.0f;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------
@@ -836,6 +864,13 @@ hipError_t launch_degree_order(const int32_t* deg, int n, const int32_t* row_ptr
   return hipGetLastError();
 }
 
+hipError_t launch_zero_inactive(const int32_t* row_ptr, const uint8_t* mask, const float* gate, int n_nodes,
+                                float* grad_w, int w_stride, hipStream_t s) {
+  if (n_nodes == 0 || !grad_w || (!mask && !gate)) return hipSuccess;
+  zero_inactive_kernel<<<ceil_div(n_nodes, 4), 256, 0, s>>>(row_ptr, mask, gate, n_nodes, grad_w, w_stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int32_t* act_row_ptr, int n_nodes,
                           int n_edges, int32_t* act_eid, hipStream_t s) {
   if (n_edges == 0 || n_nodes == 0) return hipSuccess;
@@ -874,5 +909,19 @@ hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hi
 static_assert(kNumClassesF64 == 7, "launch_conv covers every fp64 kernel class");
 
 static_assert(kNumClasses == 9, "launch_conv covers every kernel class");
+
+hipError_t launch_conv_bwd(const ConvArgsT<float>& args, int cls, hipStream_t s) {
+  switch (cls) {
+    case 0: return launch_conv_bwd_class<0>(args, s);
+    case 1: return launch_conv_bwd_class<1>(args, s);
+    case 2: return launch_conv_bwd_class<2>(args, s);
+    case 3: return launch_conv_bwd_class<3>(args, s);
+    case 4: return launch_conv_bwd_class<4>(args, s);
+    case 5: return launch_conv_bwd_class<5>(args, s);
+    case 6: return launch_conv_bwd_class<6>(args, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+static_assert(kNumClassesBwd == 7, "launch_conv_bwd covers every class with l <= kBwdLmax");
 
 }  // namespace cgtp

@@ -59,6 +59,17 @@ hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int
 // ev_start / ev_stop (may be null): HIP events stamped at this launch's start / end.
 template <int C, typename T>
 hipError_t launch_conv_class(const ConvArgsT<T>& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
+// The backward's edge pass over the same launch (args.grad_out, grad_w (may be null),
+// gyp, job_gy, scratch_row set): the w-gradient of every active edge and the per-job
+// dL/dY of every active slot.  Classes 0 .. kNumClassesBwd - 1.
+template <int C>
+hipError_t launch_conv_bwd_class(const ConvArgsT<float>& args, hipStream_t s);
+hipError_t launch_conv_bwd(const ConvArgsT<float>& args, int cls, hipStream_t s);
+constexpr int kNumClassesBwd = 7;
+// Zeroes the w-gradient rows [n_edges, w_stride] of the inactive edges (mask == 0 or
+// gate == 0; mask and gate may each be null).
+hipError_t launch_zero_inactive(const int32_t* row_ptr, const uint8_t* mask, const float* gate, int n_nodes,
+                                float* grad_w, int w_stride, hipStream_t s);
 hipError_t launch_conv(const ConvArgsT<float>& args, int cls, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hipEvent_t ev_start,
                        hipEvent_t ev_stop);
@@ -66,11 +77,7 @@ hipError_t launch_conv(const ConvArgsT<double>& args, int cls, hipStream_t s, hi
 // Largest l of a plan that the backward supports.
 constexpr int kBwdLmax = 4;
 
-// Backward of the convolution (fp32, plans with l <= kBwdLmax).  bwd_edges: w-gradient of every
-// edge (zero rows for inactive ones) and, when want_gy, the per-path dL/dY partial of
-// every active slot; one wave per (receiver, path).  high: the plan has paths of
-// l = kBwdLmax (they run in a second launch, built apart from the l <= 3 code).
-hipError_t launch_bwd_edges(const BwdArgs& a, bool high, hipStream_t s);
+
 // Active slots grouped by sender: t_row_ptr [n+1], t_slot / t_recv [active edges], each
 // sender's entries in slot order.  t_cnt: [n] scratch.
 hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,

@@ -244,9 +244,11 @@ int cgtp_backward_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_ed
  * differentiated), cell and shifts are constants; inactive edges contribute nothing
  * and their w and x_j are never read.  fp32 plans whose largest l is 4 or less (else
  * CGTP_ERR_UNSUPPORTED; an fp64 plan gives CGTP_ERR_INVALID_ARG).  Other arguments as
- * cgtp_conv_forward_gated; 4-byte aligned pointers; workspace at least
- * cgtp_backward_workspace_size.  Asynchronous on `stream`; results are bitwise
- * reproducible (no floating-point atomics). */
+ * cgtp_conv_forward_gated; x, w, grad_out and grad_w 16-byte aligned (the edge pass
+ * moves them in 16-byte vectors), the other pointers 4-byte aligned; x smaller than
+ * 4 GiB; workspace at least cgtp_backward_workspace_size (256-byte aligned).
+ * Asynchronous on `stream`; results are bitwise reproducible (no floating-point
+ * atomics). */
 int cgtp_conv_backward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, const float cell[9],
                        const int32_t* row_ptr, const int32_t* col, const int8_t* shift,
                        int64_t n_edges, const float* x, const float* w, const uint8_t* mask,

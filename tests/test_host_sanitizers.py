@@ -20,7 +20,7 @@ CLANG = "/opt/rocm/llvm/bin/clang++"
 
 
 def _objects():
-    names = ["kernels_graph.o", "kernels_bwd_p0.o", "kernels_bwd_p1.o"] + [f"kernels_conv_c{c}.o" for c in range(9)]
+    names = ["kernels_graph.o", "kernels_bwd.o"] + [f"kernels_conv_c{c}.o" for c in range(9)]
     return [os.path.join(BUILD, n) for n in names]
 
 
