@@ -164,6 +164,42 @@ using namespace cgtp;
 // process gets by default
 constexpr int kAuxStreams = 3;
 
+// Launches of the fused conv kernel: a kernel class, a range of its groups and the
+// workgroup's waves (its largest group's jobs plus the producer).  Launches write disjoint
+// output columns and only read the inputs, so the forward spreads them over the caller's
+// stream (stream 0) and up to kAuxStreams streams of the plan (stream k = aux stream
+// k - 1), forked from and joined back into the caller's stream by events; the small
+// latency-bound launches of the l >= 4 classes then run beside the large one.
+struct ConvLaunch {
+  int cls, g0, g1, stream, waves;
+};
+// per group: its heaviest job's cost (per-step work of a lane), its work (cost times
+// lanes, summed over its jobs) and its weight columns
+struct GroupLoad {
+  double max_cost, work, cols;
+};
+// One schedule of the plan's jobs into groups of at most jobs_per_group[class] jobs: the
+// forward's and the backward's edge pass's (at most kConvJobsBwd: the jobs whose
+// x-gradients its LDS hand-off adds).  In the forward the l <= 3 class (class 1) takes
+// groups of up to kConvJobsFwd jobs, so that one producer wave gathers each sender's
+// x_j segment (up to 7 components per channel) for all paths of its input irrep; the
+// other classes keep groups of kConvJobsBwd, as more and smaller workgroups measured
+// faster there.  Conv kernel time, groups of 3 against groups of 7: c1_768 (l <= 2)
+// 27.1 against 28.0 us; highl_768 (mostly the l >= 4 classes, whose few hundred
+// workgroups are bound by their arithmetic and edge chains) 414 against 470 us; for
+// l <= 3, c2_768 56.2 against 51.3 us and si_mask 108.3 against 105.0 us.
+struct Schedule {
+  int jobs_per_group[kNumClasses] = {};
+  std::vector<Job> jobs;             // ordered by group
+  std::vector<Group> groups;         // by kernel class, heavy groups first
+  std::vector<int> class_begin;      // [kNumClasses + 1] first group of each class
+  std::vector<GroupLoad> group_load;
+  std::vector<ConvLaunch> launches;  // in enqueue order
+  int n_variants = 0;
+  int n_aux = 0;                     // streams beside the caller's that the launches use
+  Job* d_jobs = nullptr;             // device copy of jobs
+};
+
 struct cgtp_plan_s {
   std::vector<Irrep> in, sh, out;
   std::vector<PathInfo> paths;
@@ -173,50 +209,30 @@ struct cgtp_plan_s {
   int sh_pad = 4;                    // elements per SH row of the forward workspace (16-byte rows)
   int elem = 4;                      // bytes per element of x, w, out and the workspace SH
   std::string irreps_out;
-  std::vector<Job> jobs;             // ordered by group
-  std::vector<Group> groups;         // by kernel class, heavy groups first
-  std::vector<int> class_begin;      // [kNumClasses + 1] first group of each class
-  int n_variants = 0;
+  Schedule fwd, bwd;                 // the forward's and the backward edge pass's schedules
   bool host_only = true;
   int device = -1;
-  void* d_tables = nullptr;          // device copy of the job, path and irrep tables
-  Job* d_jobs = nullptr;
-  // backward tables: one record per path, and the paths of each input irrep as
-  // [start (n_in + 1) | paths (n_paths) | l (n_in) | mul (n_in) | offset (n_in)]
-  std::vector<PathDev> pdev;
-  std::vector<int32_t> irrep_tab;
-  int gy_stride = 0;                 // sum over paths of 2 l2 + 1
-  int xp_stride = 0;                 // sum over paths of mul (2 l1 + 1)
+  void* d_tables = nullptr;          // device copy of the job tables and the backward tables
   int lmax = 0;                      // largest l of the plan
-  PathDev* d_paths = nullptr;
-  int32_t* d_irrep = nullptr;
-  // the backward edge pass's dL/dY partials: per job (a path and channel block) a block
-  // of 2 l2 + 1 values in a row of gy_stride (job order), and the {l2, offset} list of the
-  // blocks that the force pass adds
-  std::vector<int32_t> job_gy;
-  std::vector<int2> gy_list;
-  int32_t* d_job_gy = nullptr;
-  int2* d_gy_list = nullptr;
-  // Forward launches: a kernel class and a range of its groups each.  Launches write
-  // disjoint output columns and only read the inputs, so the plan spreads them over the
-  // caller's stream (stream 0) and up to kAuxStreams streams of its own (stream k = aux
-  // stream k - 1), forked from and joined back into the caller's stream by events; the
-  // small latency-bound launches of the l >= 4 classes then run beside the large one.
-  struct ConvLaunch {
-    int cls, g0, g1, stream;
-  };
-  // per group: its heaviest job's cost (per-step work of a lane), its work (cost times
-  // lanes, summed over its jobs) and its weight columns
-  struct GroupLoad {
-    double max_cost, work, cols;
-  };
-  std::vector<GroupLoad> group_load;
-  std::vector<ConvLaunch> launches;  // in enqueue order
-  int n_aux = 0;
-  hipStream_t aux[kAuxStreams] = {};
+  // backward tables.  A row of the edge pass's partials (one per active slot) holds
+  // [each job's dL/dY block (2 l2 + 1, job order) | padding to 4 | each group's
+  // x-gradient block (n_ch (2 l1 + 1) in x's layout, padded to 4; group order)], jobs
+  // and groups of the backward's schedule;
+  // job_gy / job_xg give each job's block (a group's jobs share one x-gradient block).
+  // xcol: per column of x, the row entries of the blocks that read it (CSR, group
+  // order); ycol: per harmonic component, the entries of its jobs' dL/dY (job order).
+  int part_stride = 0;
+  std::vector<int32_t> job_gy, job_xg, xcol_ptr, xcol_off, ycol_ptr, ycol_off;
+  int32_t *d_job_gy = nullptr, *d_job_xg = nullptr;
+  int32_t *d_xcol_ptr = nullptr, *d_xcol_off = nullptr, *d_ycol_ptr = nullptr, *d_ycol_off = nullptr;
+  hipStream_t aux[kAuxStreams] = {};   // the forward's streams beside the caller's
   hipEvent_t fork = nullptr;
   hipEvent_t join[kAuxStreams] = {};
-  std::mutex enqueue;                // held while a forward forks, launches and joins
+  // the backward's side stream (fp32 plans with l <= kBwdLmax): the zeroing of inactive
+  // w-gradient rows and the grouping of slots by sender run on it beside the edge pass
+  hipStream_t bwd_side = nullptr;
+  hipEvent_t bwd_ev[2] = {};
+  std::mutex enqueue;                // held while a forward or backward forks, launches and joins
 };
 
 namespace {
@@ -225,12 +241,13 @@ namespace {
 // 16-byte aligned, else K = 1; lanes per receiver = next power of two of mul/K, at most
 // 64 (larger multiplicities are cut into channel blocks of 64*K).  Jobs of one kernel
 // class, input irrep, channel block and K form a set that shares x_j rows; each set is
-// cut into groups of at most kConvJobs jobs, one workgroup per group and node group.
+// cut into groups of at most S.jobs_per_group[class] jobs, one workgroup per group and
+// node group.
 // Jobs keep their weight-column order inside a set, so that a group's consumers read
 // adjacent columns of each weight row; groups are ordered heaviest first inside a class
 // (LunaTP Table 9: ordering by descending CG-term count was fastest).
-void schedule(cgtp_plan_s& P) {
-  P.jobs.clear();
+void schedule(const cgtp_plan_s& P, Schedule& S) {
+  S.jobs.clear();
   struct Tmp {
     Job j;
     int cls, irrep, block, l2;
@@ -300,8 +317,13 @@ void schedule(cgtp_plan_s& P) {
     while (e < tmp.size() && tmp[b].cls == tmp[e].cls && tmp[b].irrep == tmp[e].irrep &&
            tmp[b].block == tmp[e].block && variant_desc(tmp[b].j.variant).k == variant_desc(tmp[e].j.variant).k)
       ++e;
-    // cut the set [b, e) into ceil(n / kConvJobs) groups of balanced size
-    const int n = int(e - b), ng = (n + kConvJobs - 1) / kConvJobs;
+    // cut the set [b, e) into ceil(n / jobs_per_group) groups of balanced size
+    // large groups only where a workgroup serves several receivers (fewer than 64 lanes
+    // per receiver): with one receiver per workgroup its chain is that receiver's whole
+    // edge list, which more and smaller groups shorten (c4_768, 256 channels: 141.5
+    // against 151.2 us)
+    const int jpg = tmp[b].j.lanes_log2 < 6 ? S.jobs_per_group[tmp[b].cls] : kConvJobsBwd;
+    const int n = int(e - b), ng = (n + jpg - 1) / jpg;
     int at = int(b);
     for (int g = 0; g < ng; ++g) {
       const int sz = n / ng + (g < n % ng ? 1 : 0);
@@ -316,17 +338,17 @@ void schedule(cgtp_plan_s& P) {
     if (x.cls != y.cls) return x.cls < y.cls;
     return x.cost > y.cost;
   });
-  P.groups.clear();
-  P.group_load.clear();
-  P.class_begin.assign(kNumClasses + 1, 0);
+  S.groups.clear();
+  S.group_load.clear();
+  S.class_begin.assign(kNumClasses + 1, 0);
   for (const G& g : gs) {
     Group G{};
-    G.first_job = int(P.jobs.size());
+    G.first_job = int(S.jobs.size());
     G.n_jobs = g.n;
     G.lanes_log2 = tmp[g.begin].j.lanes_log2;
     int l2lo = kMaxL, l2hi = 0;
     for (int k = g.begin; k < g.begin + g.n; ++k) {
-      P.jobs.push_back(tmp[k].j);
+      S.jobs.push_back(tmp[k].j);
       l2lo = std::min(l2lo, tmp[k].l2);
       l2hi = std::max(l2hi, tmp[k].l2);
     }
@@ -335,19 +357,19 @@ void schedule(cgtp_plan_s& P) {
     // at least y4 lanes per receiver, so that the S y4 harmonic chunks of a step fit the
     // producer wave's 64 lanes (extra lanes idle)
     G.lanes_log2 = std::max(G.lanes_log2, ilog2(next_pow2(G.y4)));
-    for (int k = G.first_job; k < G.first_job + G.n_jobs; ++k) P.jobs[k].lanes_log2 = G.lanes_log2;
-    P.groups.push_back(G);
+    for (int k = G.first_job; k < G.first_job + G.n_jobs; ++k) S.jobs[k].lanes_log2 = G.lanes_log2;
+    S.groups.push_back(G);
     double work = 0.0, cols = 0.0;
     for (int k = g.begin; k < g.begin + g.n; ++k) {
       work += tmp[k].cost * tmp[k].j.n_ch / (64.0 * variant_desc(tmp[k].j.variant).k);
       cols += tmp[k].j.n_ch;
     }
-    P.group_load.push_back({g.cost, work, cols});
-    P.class_begin[g.cls + 1]++;
+    S.group_load.push_back({g.cost, work, cols});
+    S.class_begin[g.cls + 1]++;
   }
-  for (int c = 0; c < kNumClasses; ++c) P.class_begin[c + 1] += P.class_begin[c];
-  P.n_variants = 0;
-  for (int u : used) P.n_variants += u;
+  for (int c = 0; c < kNumClasses; ++c) S.class_begin[c + 1] += S.class_begin[c];
+  S.n_variants = 0;
+  for (int u : used) S.n_variants += u;
 
   // launches of up to kMaxGroupsPerLaunch groups of one class, spread over the streams
   // longest first onto the least loaded (the first, the longest, stays on the caller's
@@ -355,37 +377,42 @@ void schedule(cgtp_plan_s& P) {
   // microseconds for a graph of about 20 000 edges (only their ratios matter): the
   // receiver with the most edges walks them in sequence at a step time set by the
   // heaviest group, the arithmetic of all groups, and the weight stream.
-  P.launches.clear();
+  S.launches.clear();
   for (int c = 0; c < kNumClasses; ++c)
-    for (int g0 = P.class_begin[c]; g0 < P.class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
-      P.launches.push_back({c, g0, std::min(P.class_begin[c + 1], g0 + kMaxGroupsPerLaunch), 0});
-  std::vector<double> est(P.launches.size(), 0.0);
-  for (size_t li = 0; li < P.launches.size(); ++li) {
+    for (int g0 = S.class_begin[c]; g0 < S.class_begin[c + 1]; g0 += kMaxGroupsPerLaunch)
+      S.launches.push_back({c, g0, std::min(S.class_begin[c + 1], g0 + kMaxGroupsPerLaunch), 0, 0});
+  for (ConvLaunch& L : S.launches) {
+    int most = 1;
+    for (int k = L.g0; k < L.g1; ++k) most = std::max(most, S.groups[k].n_jobs);
+    L.waves = most + 1;
+  }
+  std::vector<double> est(S.launches.size(), 0.0);
+  for (size_t li = 0; li < S.launches.size(); ++li) {
     double chain = 0.0, work = 0.0, cols = 0.0;
-    for (int k = P.launches[li].g0; k < P.launches[li].g1; ++k) {
-      chain = std::max(chain, P.group_load[k].max_cost);
-      work += P.group_load[k].work;
-      cols += P.group_load[k].cols;
+    for (int k = S.launches[li].g0; k < S.launches[li].g1; ++k) {
+      chain = std::max(chain, S.group_load[k].max_cost);
+      work += S.group_load[k].work;
+      cols += S.group_load[k].cols;
     }
     est[li] = std::max(10.0 + 0.075 * chain, std::max(0.072 * work, 0.026 * cols));
   }
-  std::vector<int> ord(P.launches.size());
+  std::vector<int> ord(S.launches.size());
   for (size_t li = 0; li < ord.size(); ++li) ord[li] = int(li);
   std::stable_sort(ord.begin(), ord.end(), [&](int x, int y) { return est[x] > est[y]; });
   double load[kAuxStreams + 1] = {};
-  std::vector<cgtp_plan_s::ConvLaunch> sorted;
-  P.n_aux = 0;
+  std::vector<ConvLaunch> sorted;
+  S.n_aux = 0;
   for (int li : ord) {
     int best = 0;
     for (int k = 1; k <= kAuxStreams; ++k)
       if (load[k] < load[best]) best = k;
     load[best] += est[li];
-    cgtp_plan_s::ConvLaunch L = P.launches[li];
+    ConvLaunch L = S.launches[li];
     L.stream = best;
-    P.n_aux = std::max(P.n_aux, best);
+    S.n_aux = std::max(S.n_aux, best);
     sorted.push_back(L);
   }
-  P.launches = sorted;
+  S.launches = sorted;
 }
 
 
@@ -441,6 +468,9 @@ void release_device(cgtp_plan_s* P) {
     if (P->join[k]) (void)hipEventDestroy(P->join[k]);
   }
   if (P->fork) (void)hipEventDestroy(P->fork);
+  if (P->bwd_side) (void)hipStreamDestroy(P->bwd_side);
+  for (hipEvent_t ev : P->bwd_ev)
+    if (ev) (void)hipEventDestroy(ev);
   P->d_tables = nullptr;
 }
 
@@ -550,58 +580,48 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     }
   }
   P->irreps_out = format_irreps(P->out);
-  schedule(*P);
+  for (int c = 0; c < kNumClasses; ++c) {
+    P->fwd.jobs_per_group[c] = c == 1 ? kConvJobsFwd : kConvJobsBwd;
+    P->bwd.jobs_per_group[c] = kConvJobsBwd;
+  }
+  schedule(*P, P->fwd);
+  schedule(*P, P->bwd);
   // backward tables
-  P->gy_stride = 0;
-  P->xp_stride = 0;
   P->lmax = 0;
-  for (const PathInfo& p : P->paths) {
-    PathDev d{};
-    d.variant = variant_index(p.l1, p.l2, p.l3, 1);
-    d.l1 = p.l1;
-    d.l2 = p.l2;
-    d.l3 = p.l3;
-    d.mul = p.mul;
-    d.in_off = p.in_off;
-    d.out_off = p.out_off;
-    d.w_off = p.w_off;
-    d.sh_off = p.l2 * p.l2;
-    d.gy_off = P->gy_stride;
-    d.i_in = p.i_in;
-    d.xp_off = P->xp_stride;
-    P->gy_stride += 2 * p.l2 + 1;
-    P->xp_stride += p.mul * (2 * p.l1 + 1);
-    P->lmax = std::max(P->lmax, std::max(p.l1, std::max(p.l2, p.l3)));
-    P->pdev.push_back(d);
-  }
-  P->gy_stride = 0;
-  for (const Job& j : P->jobs) {
-    const int l2 = variant_desc(j.variant).l2;
-    P->job_gy.push_back(P->gy_stride);
-    P->gy_list.push_back(make_int2(l2, P->gy_stride));
-    P->gy_stride += 2 * l2 + 1;
-  }
+  for (const PathInfo& p : P->paths) P->lmax = std::max(P->lmax, std::max(p.l1, std::max(p.l2, p.l3)));
   {
-    const int ni = int(P->in.size());
-    std::vector<int32_t> start(ni + 1, 0), list;
-    for (int a = 0; a < ni; ++a) {
-      for (size_t q = 0; q < P->paths.size(); ++q)
-        if (P->paths[q].i_in == a) list.push_back(int32_t(q));
-      start[a + 1] = int32_t(list.size());
+    auto pad4 = [](int v) { return (v + 3) & ~3; };
+    int at = 0;
+    const Schedule& B = P->bwd;
+    for (const Job& j : B.jobs) {
+      P->job_gy.push_back(at);
+      at += 2 * variant_desc(j.variant).l2 + 1;
     }
-    P->irrep_tab = start;
-    P->irrep_tab.insert(P->irrep_tab.end(), list.begin(), list.end());
-    int64_t off_in = 0;
-    std::vector<int32_t> ls, ms, os;
-    for (const Irrep& r : P->in) {
-      ls.push_back(r.l);
-      ms.push_back(r.mul);
-      os.push_back(int32_t(off_in));
-      off_in += int64_t(r.mul) * (2 * r.l + 1);
+    at = pad4(at);
+    P->job_xg.assign(B.jobs.size(), 0);
+    std::vector<std::vector<int32_t>> xcover(size_t(P->f_in)), ycover(size_t(P->sh_stride));
+    for (const Group& G : B.groups) {
+      const Job& J = B.jobs[G.first_job];
+      const int n1 = 2 * variant_desc(J.variant).l1 + 1, len = J.n_ch * n1;
+      for (int k = G.first_job; k < G.first_job + G.n_jobs; ++k) P->job_xg[k] = at;
+      for (int c = 0; c < len; ++c) xcover[size_t(J.in_off + c)].push_back(at + c);
+      at += pad4(len);
     }
-    P->irrep_tab.insert(P->irrep_tab.end(), ls.begin(), ls.end());
-    P->irrep_tab.insert(P->irrep_tab.end(), ms.begin(), ms.end());
-    P->irrep_tab.insert(P->irrep_tab.end(), os.begin(), os.end());
+    P->part_stride = at;
+    for (size_t k = 0; k < B.jobs.size(); ++k) {
+      const int l2 = variant_desc(B.jobs[k].variant).l2;
+      for (int m = 0; m < 2 * l2 + 1; ++m) ycover[size_t(l2 * l2 + m)].push_back(P->job_gy[k] + m);
+    }
+    auto flatten = [](const std::vector<std::vector<int32_t>>& cov, std::vector<int32_t>& ptr,
+                      std::vector<int32_t>& off) {
+      ptr.assign(1, 0);
+      for (const auto& v : cov) {
+        off.insert(off.end(), v.begin(), v.end());
+        ptr.push_back(int32_t(off.size()));
+      }
+    };
+    flatten(xcover, P->xcol_ptr, P->xcol_off);
+    flatten(ycover, P->ycol_ptr, P->ycol_off);
   }
 
   P->host_only = (flags & CGTP_PLAN_HOST_ONLY) != 0;
@@ -619,35 +639,43 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
       return fail(CGTP_ERR_NO_DEVICE, "current device is not gfx950");
     }
     P->device = dev;
-    const size_t jb = align256(P->jobs.size() * sizeof(Job));
-    const size_t pb = align256(P->pdev.size() * sizeof(PathDev));
-    const size_t ib = align256(P->irrep_tab.size() * sizeof(int32_t));
-    const size_t gb = align256(P->job_gy.size() * sizeof(int32_t));
-    const size_t lb = P->gy_list.size() * sizeof(int2);
-    hipError_t e = hipMalloc(&P->d_tables, jb + pb + ib + gb + lb);
+    // one allocation: the two job tables, then the backward tables, each 256-byte aligned
+    const std::vector<int32_t>* tabs[] = {&P->job_gy, &P->job_xg, &P->xcol_ptr, &P->xcol_off, &P->ycol_ptr,
+                                          &P->ycol_off};
+    int32_t** dtabs[] = {&P->d_job_gy, &P->d_job_xg, &P->d_xcol_ptr, &P->d_xcol_off, &P->d_ycol_ptr,
+                         &P->d_ycol_off};
+    Schedule* scheds[] = {&P->fwd, &P->bwd};
+    size_t total = 0;
+    for (const Schedule* S : scheds) total += align256(S->jobs.size() * sizeof(Job));
+    for (const auto* t : tabs) total += align256(std::max<size_t>(t->size(), 1) * sizeof(int32_t));
+    hipError_t e = hipMalloc(&P->d_tables, total);
     if (e == hipSuccess) {
       char* base = static_cast<char*>(P->d_tables);
-      P->d_jobs = reinterpret_cast<Job*>(base);
-      P->d_paths = reinterpret_cast<PathDev*>(base + jb);
-      P->d_irrep = reinterpret_cast<int32_t*>(base + jb + pb);
-      P->d_job_gy = reinterpret_cast<int32_t*>(base + jb + pb + ib);
-      P->d_gy_list = reinterpret_cast<int2*>(base + jb + pb + ib + gb);
-      e = hipMemcpy(P->d_jobs, P->jobs.data(), P->jobs.size() * sizeof(Job), hipMemcpyHostToDevice);
-      if (e == hipSuccess)
-        e = hipMemcpy(P->d_paths, P->pdev.data(), P->pdev.size() * sizeof(PathDev), hipMemcpyHostToDevice);
-      if (e == hipSuccess)
-        e = hipMemcpy(P->d_irrep, P->irrep_tab.data(), P->irrep_tab.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-      if (e == hipSuccess)
-        e = hipMemcpy(P->d_job_gy, P->job_gy.data(), P->job_gy.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-      if (e == hipSuccess) e = hipMemcpy(P->d_gy_list, P->gy_list.data(), lb, hipMemcpyHostToDevice);
+      size_t off = 0;
+      for (Schedule* S : scheds) {
+        S->d_jobs = reinterpret_cast<Job*>(base + off);
+        if (e == hipSuccess)
+          e = hipMemcpy(S->d_jobs, S->jobs.data(), S->jobs.size() * sizeof(Job), hipMemcpyHostToDevice);
+        off += align256(S->jobs.size() * sizeof(Job));
+      }
+      for (int k = 0; k < 6 && e == hipSuccess; ++k) {
+        *dtabs[k] = reinterpret_cast<int32_t*>(base + off);
+        if (!tabs[k]->empty())
+          e = hipMemcpy(*dtabs[k], tabs[k]->data(), tabs[k]->size() * sizeof(int32_t), hipMemcpyHostToDevice);
+        off += align256(std::max<size_t>(tabs[k]->size(), 1) * sizeof(int32_t));
+      }
     }
     // auxiliary streams (default priority, not synchronising with the null stream) and
     // the fork/join events of the concurrent launches
-    for (int k = 0; e == hipSuccess && k < P->n_aux; ++k) {
+    for (int k = 0; e == hipSuccess && k < P->fwd.n_aux; ++k) {
       e = hipStreamCreateWithFlags(&P->aux[k], hipStreamNonBlocking);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&P->join[k], hipEventDisableTiming);
     }
-    if (e == hipSuccess && P->n_aux > 0) e = hipEventCreateWithFlags(&P->fork, hipEventDisableTiming);
+    if (e == hipSuccess && P->fwd.n_aux > 0) e = hipEventCreateWithFlags(&P->fork, hipEventDisableTiming);
+    if (e == hipSuccess && P->elem == 4 && P->lmax <= kBwdLmax) {
+      e = hipStreamCreateWithFlags(&P->bwd_side, hipStreamNonBlocking);
+      for (int k = 0; e == hipSuccess && k < 2; ++k) e = hipEventCreateWithFlags(&P->bwd_ev[k], hipEventDisableTiming);
+    }
     if (e != hipSuccess) {
       release_device(P);
       delete P;
@@ -655,8 +683,8 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     }
   }
   log_line(2, "plan %s x %s -> %s: %zu paths, %zu jobs, %zu groups, %zu launches on %d streams%s",
-           irreps_in, irreps_sh, P->irreps_out.c_str(), P->paths.size(), P->jobs.size(), P->groups.size(),
-           P->launches.size(), P->n_aux + 1, P->host_only ? " (host only)" : "");
+           irreps_in, irreps_sh, P->irreps_out.c_str(), P->paths.size(), P->fwd.jobs.size(), P->fwd.groups.size(),
+           P->fwd.launches.size(), P->fwd.n_aux + 1, P->host_only ? " (host only)" : "");
   *out = P;
   return ok();
 }
@@ -710,8 +738,8 @@ int cgtp_plan_cg(cgtp_plan_t P, int path, float* dense) {
 
 int cgtp_plan_schedule(cgtp_plan_t P, int* n_jobs, int* n_variants) {
   if (!P) return fail(CGTP_ERR_INVALID_ARG, "plan is NULL");
-  if (n_jobs) *n_jobs = int(P->jobs.size());
-  if (n_variants) *n_variants = P->n_variants;
+  if (n_jobs) *n_jobs = int(P->fwd.jobs.size());
+  if (n_variants) *n_variants = P->fwd.n_variants;
   return ok();
 }
 
@@ -836,14 +864,14 @@ int cgtp_edge_sh(cgtp_plan_t P, const float* pos, int64_t n_nodes, const float c
 // groups of every group g, so the groups of one block, which read the same weight rows,
 // run at the same time.
 template <typename T>
-static int64_t fill_launch(const cgtp_plan_s& P, const cgtp_plan_s::ConvLaunch& L, int64_t n_nodes, ConvArgsT<T>& a) {
+static int64_t fill_launch(const Schedule& S, const ConvLaunch& L, int64_t n_nodes, ConvArgsT<T>& a) {
   a.n_groups = L.g1 - L.g0;
   for (int k = 0; k < kMaxGroupsPerLaunch; ++k) a.g_start[k] = kMaxInt32;   // past the groups
   int lg_min = 6;
-  for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, P.groups[k].lanes_log2);
+  for (int k = L.g0; k < L.g1; ++k) lg_min = std::min(lg_min, S.groups[k].lanes_log2);
   int per_block = 0;
   for (int k = L.g0; k < L.g1; ++k) {
-    const Group& G = P.groups[k];
+    const Group& G = S.groups[k];
     a.g_start[k - L.g0] = per_block;
     GroupArgs& ga = a.grp[k - L.g0];
     ga.start = per_block;
@@ -858,6 +886,8 @@ static int64_t fill_launch(const cgtp_plan_s& P, const cgtp_plan_s::ConvLaunch& 
   const int64_t nblocks = (n_nodes + block - 1) / block;
   // whole rounds of kXcds blocks: blocks past the last are empty workgroups
   const int64_t wgs = (nblocks + kXcds - 1) / kXcds * kXcds * per_block;
+  a.jobs = S.d_jobs;
+  a.n_waves = L.waves;
   a.blk_wgs = per_block;
   a.blk_lg_min = lg_min;
   a.n_blocks = int(nblocks);
@@ -932,26 +962,26 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
   a.act_e = ws.act_e;
   a.act_j = ws.act_j;
   a.out = out;
-  a.jobs = P->d_jobs;
   a.n_nodes = int(n_nodes);
   a.f_in = int(P->f_in);
   a.f_out = int(P->f_out);
   a.w_stride = int(P->w);
   a.sh_stride = P->sh_pad;
-  auto fill = [&](const cgtp_plan_s::ConvLaunch& L) -> int64_t { return fill_launch(*P, L, n_nodes, a); };
-  const auto& launches = P->launches;
+  const Schedule& F = P->fwd;
+  auto fill = [&](const ConvLaunch& L) -> int64_t { return fill_launch(F, L, n_nodes, a); };
+  const auto& launches = F.launches;
   for (const auto& L : launches)
     if (fill(L) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
   // With auxiliary streams: fork them from the caller's stream after the per-row pass,
   // launch, and join them back; the events then bracket the whole set (enqueue-time
   // records).  On one stream the events are stamped by the first and last launches.
-  const bool forked = P->n_aux > 0;
+  const bool forked = F.n_aux > 0;
   std::unique_lock<std::mutex> lock(P->enqueue, std::defer_lock);
   if (forked) {
     lock.lock();
     if (ev_begin) CGTP_HIP(hipEventRecord(ev_begin, s));
     CGTP_HIP(hipEventRecord(P->fork, s));
-    for (int k = 0; k < P->n_aux; ++k) CGTP_HIP(hipStreamWaitEvent(P->aux[k], P->fork, 0));
+    for (int k = 0; k < F.n_aux; ++k) CGTP_HIP(hipStreamWaitEvent(P->aux[k], P->fork, 0));
   }
   hipError_t launch_err = hipSuccess;
   for (size_t li = 0; li < launches.size() && launch_err == hipSuccess; ++li) {
@@ -962,7 +992,7 @@ static int conv_forward_impl(cgtp_plan_t P, const T* pos, int64_t n_nodes, const
                              !forked && li + 1 == launches.size() ? ev_end : nullptr);
   }
   if (forked) {   // joined even after a failed launch, so that `stream` follows what ran
-    for (int k = 0; k < P->n_aux; ++k) {
+    for (int k = 0; k < F.n_aux; ++k) {
       CGTP_HIP(hipEventRecord(P->join[k], P->aux[k]));
       CGTP_HIP(hipStreamWaitEvent(s, P->join[k], 0));
     }
@@ -1051,11 +1081,11 @@ extern "C" int cgtp_conv_forward_noalloc(cgtp_plan_t P, const float* pos, int64_
 }
 
 // Workspace of the backward: the forward's sections, then the sender-grouped slots, the
-// per-path dL/dY partials and dL/dr per slot.
+// edge pass's rows of partials (one per slot) and dL/dr per slot.
 struct BwdWorkspace {
   FwdWorkspace fwd;
   int32_t *t_cnt, *t_row_ptr, *t_slot, *t_recv;
-  float *gyp, *grad_r, *xp;
+  float *part, *grad_r;
   float* scratch_row;   // the edge pass's stores of lanes with nothing to store
   size_t bytes;
 };
@@ -1074,9 +1104,8 @@ static BwdWorkspace carve_bwd(const cgtp_plan_s& P, int64_t n, int64_t e, void* 
   w.t_row_ptr = reinterpret_cast<int32_t*>(take(size_t(n + 1) * 4));
   w.t_slot = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
   w.t_recv = reinterpret_cast<int32_t*>(take(size_t(e) * 4));
-  w.gyp = reinterpret_cast<float*>(take(size_t(e) * size_t(P.gy_stride) * 4));
+  w.part = reinterpret_cast<float*>(take(size_t(e) * size_t(P.part_stride) * 4));
   w.grad_r = reinterpret_cast<float*>(take(size_t(e) * 12));
-  w.xp = reinterpret_cast<float*>(take(size_t(n) * size_t(P.xp_stride) * 4));
   w.scratch_row = reinterpret_cast<float*>(take(64 * 4));
   w.bytes = off;
   return w;
@@ -1139,55 +1168,45 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
     CGTP_HIP(launch_rows(g, P->l_sh_max, s));
     CGTP_HIP(launch_degree_order(ws.fwd.deg, int(n_nodes), row_ptr, ws.fwd.node_info, s));
   }
+  // 2. beside the edge pass, on the plan's side stream: the zeroing of the inactive
+  //    edges' w-gradient rows and the grouping of the active slots by sender
   BwdArgs a{};
-  a.x = x;
-  a.w = w;
-  a.sh = static_cast<const float*>(ws.fwd.sh);
-  a.grad_out = grad_out;
   a.pos = pos;
   a.row_ptr = row_ptr;
   a.shift = shift;
-  a.mask = mask;
   a.gate = gate;
   a.deg = ws.fwd.deg;
   a.act_e = ws.fwd.act_e;
   a.act_j = ws.fwd.act_j;
-  a.paths = P->d_paths;
-  const int ni = int(P->in.size()), np = int(P->paths.size());
-  a.irrep_start = P->d_irrep;
-  a.irrep_paths = P->d_irrep + ni + 1;
-  a.irrep_l = P->d_irrep + ni + 1 + np;
-  a.irrep_mul = a.irrep_l + ni;
-  a.irrep_off = a.irrep_mul + ni;
   a.t_row_ptr = ws.t_row_ptr;
   a.t_slot = ws.t_slot;
   a.t_recv = ws.t_recv;
+  a.part = ws.part;
+  a.xcol_ptr = P->d_xcol_ptr;
+  a.xcol_off = P->d_xcol_off;
+  a.ycol_ptr = P->d_ycol_ptr;
+  a.ycol_off = P->d_ycol_off;
   a.grad_x = grad_x;
-  a.grad_w = grad_w;
-  a.gyp = ws.gyp;
-  a.gy_list = P->d_gy_list;
-  a.n_gy = int(P->gy_list.size());
   a.grad_r = ws.grad_r;
-  a.xp = ws.xp;
-  a.xp_stride = P->xp_stride;
   a.grad_pos = grad_pos;
   a.n_nodes = int(n_nodes);
-  a.n_paths = np;
-  a.n_irreps = ni;
   a.f_in = int(P->f_in);
-  a.f_out = int(P->f_out);
-  a.w_stride = int(P->w);
-  a.sh_stride = P->sh_pad;
-  a.gy_stride = P->gy_stride;
+  a.part_stride = P->part_stride;
   a.l_sh_max = P->l_sh_max;
   a.want_gy = grad_pos != nullptr;
   a.has_cell = cell != nullptr;
   for (int k = 0; k < 9; ++k) a.cell[k] = cell ? double(cell[k]) : 0.0;
-  // 2. the edge pass: the fused conv kernel's workgroups in their backward mode write the
-  //    w-gradient of every active edge and the per-job dL/dY partials of every active
-  //    slot; the rows of inactive edges are zeroed apart
-  if (grad_w) CGTP_HIP(launch_zero_inactive(row_ptr, mask, gate, int(n_nodes), grad_w, int(P->w), s));
-  if (grad_w || grad_pos) {
+  std::lock_guard<std::mutex> lock(P->enqueue);
+  hipStream_t b = P->bwd_side;
+  CGTP_HIP(hipEventRecord(P->bwd_ev[0], s));
+  CGTP_HIP(hipStreamWaitEvent(b, P->bwd_ev[0], 0));
+  if (grad_w) CGTP_HIP(launch_zero_inactive(row_ptr, mask, gate, int(n_nodes), grad_w, int(P->w), b));
+  if (grad_x || grad_pos) CGTP_HIP(launch_bwd_transpose(a, ws.t_cnt, ws.t_row_ptr, ws.t_slot, ws.t_recv, b));
+  CGTP_HIP(hipEventRecord(P->bwd_ev[1], b));
+  // 3. the edge pass: the fused conv kernel's workgroups in their backward mode write the
+  //    w-gradient of every active edge and, per active slot, the jobs' dL/dY and the job
+  //    groups' x-gradients of the edge
+  {
     ConvArgsT<float> c{};
     c.x = x;
     c.w = w;
@@ -1195,7 +1214,6 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
     c.node_info = ws.fwd.node_info;
     c.act_e = ws.fwd.act_e;
     c.act_j = ws.fwd.act_j;
-    c.jobs = P->d_jobs;
     c.n_nodes = int(n_nodes);
     c.f_in = int(P->f_in);
     c.f_out = int(P->f_out);
@@ -1203,19 +1221,26 @@ int cgtp_conv_backward(cgtp_plan_t P, const float* pos, int64_t n_nodes, const f
     c.sh_stride = P->sh_pad;
     c.grad_out = grad_out;
     c.grad_w = grad_w;
-    c.gyp = grad_pos ? ws.gyp : nullptr;
+    c.gyp = grad_pos ? ws.part : nullptr;
+    c.xgp = grad_x ? ws.part : nullptr;
     c.job_gy = P->d_job_gy;
+    c.job_xg = P->d_job_xg;
     c.scratch_row = ws.scratch_row;
-    c.gy_stride = P->gy_stride;
-    for (const auto& L : P->launches) {
-      if (fill_launch(*P, L, n_nodes, c) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
+    c.part_stride = P->part_stride;
+    for (const auto& L : P->bwd.launches) {
+      if (fill_launch(P->bwd, L, n_nodes, c) > kMaxInt32) return fail(CGTP_ERR_UNSUPPORTED, "too many workgroups");
       CGTP_HIP(launch_conv_bwd(c, L.cls, s));
     }
   }
-  // 3. active slots grouped by sender, then the x-gradient and the forces
-  if (grad_x || grad_pos) CGTP_HIP(launch_bwd_transpose(a, ws.t_cnt, ws.t_row_ptr, ws.t_slot, ws.t_recv, s));
-  if (grad_x) CGTP_HIP(launch_bwd_x(a, P->lmax > 3, s));
-  if (grad_pos) CGTP_HIP(launch_bwd_pos(a, s));
+  // 4. per sender: its x-gradient and its slots' dL/dr, then the position gradient (in
+  //    the caller's stream once the side stream is joined back: run beside each other or
+  //    beside the edge pass, these passes only slowed it by as much as they took)
+  CGTP_HIP(hipStreamWaitEvent(s, P->bwd_ev[1], 0));
+  if (grad_x) CGTP_HIP(launch_bwd_gather_x(a, s));
+  if (grad_pos) {
+    CGTP_HIP(launch_bwd_force(a, s));
+    CGTP_HIP(launch_bwd_pos(a, s));
+  }
   return ok();
 }
 

@@ -28,16 +28,19 @@ struct Job {
 };
 static_assert(sizeof(Job) == 32, "Job is 32 bytes");
 
-// A group: up to kConvJobs jobs of one input irrep, one channel block, one K and one
-// kernel class, run by one workgroup per node group: one consumer wave per job and one
-// producer wave.  The jobs read the same x_j rows and the same harmonics, which the
+// A group: jobs of one input irrep, one channel block, one K and one kernel class, run by
+// one workgroup per node group: one consumer wave per job and one producer wave (the
+// workgroup's last).  The jobs read the same x_j rows and the same harmonics, which the
 // producer gathers once per edge step into LDS (LunaTP Table 8: cross-path input reuse);
-// each consumer streams only its own path's weights.
-constexpr int kConvWaves = 4;
-constexpr int kConvJobs = kConvWaves - 1;
+// each consumer streams only its own path's weights.  The forward's groups hold up to
+// kConvJobsFwd jobs; the backward's edge pass, whose LDS also carries the jobs'
+// x-gradient hand-off, up to kConvJobsBwd.
+constexpr int kConvJobsFwd = 7;
+constexpr int kConvJobsBwd = 3;
+constexpr int kConvWavesMax = kConvJobsFwd + 1;
 struct Group {
-  int32_t first_job;   // index into the plan's job table
-  int32_t n_jobs;      // 1 .. kConvJobs
+  int32_t first_job;   // index into the schedule's job table
+  int32_t n_jobs;      // 1 .. jobs per group of the schedule
   int32_t lanes_log2;  // lanes per receiver, common to the jobs
   int32_t y0;          // first harmonic (float offset in an SH row, multiple of 4) staged
   int32_t y4;          // 16-byte chunks of harmonics staged per receiver
@@ -71,15 +74,19 @@ struct ConvArgsT {
   const int32_t* act_j;       // their senders
   T* out;
   const Job* jobs;            // the plan's job table
-  // backward edge pass only (else null): dL/d out, dL/dw, the per-job dL/dY partials
-  // [slot, gy_stride] with job j's block at job_gy[j], and a scratch row for lanes with
-  // nothing to store
+  // backward edge pass only (else null): dL/d out, dL/dw, and rows of per-slot partials
+  // [active slot, part_stride]: job j's dL/dY block at job_gy[j] (written when gyp is
+  // set) and the x-gradient block of j's group at job_xg[j] (written when xgp is set;
+  // gyp and xgp both point at the rows); a scratch row for lanes with nothing to store
   const T* grad_out;
   T* grad_w;
   T* gyp;
+  T* xgp;
   const int32_t* job_gy;
+  const int32_t* job_xg;
   T* scratch_row;
-  int32_t gy_stride;
+  int32_t part_stride;
+  int32_t n_waves;            // waves of a workgroup of this launch (consumers + producer)
   int32_t n_nodes;
   int32_t f_in;
   int32_t f_out;
@@ -100,52 +107,29 @@ using ConvArgs = ConvArgsT<float>;
 constexpr int kF64Lmax = 4;
 constexpr int kNumClassesF64 = 3 + kF64Lmax;
 
-// One path of a plan, for the backward kernels (device table owned by the plan).
-struct PathDev {
-  int32_t variant;     // variant_index(l1, l2, l3, K = 1)
-  int32_t l1, l2, l3;
-  int32_t mul;
-  int32_t in_off, out_off, w_off;
-  int32_t sh_off;      // l2 * l2: the path's harmonics within an SH row
-  int32_t gy_off;      // the path's block within a row of per-path dL/dY partials
-  int32_t i_in;        // input irrep index
-  int32_t xp_off;      // the path's block within a row of per-path x-gradient partials
-};
-
 // Arguments of the backward kernels (fp32).  Active slots are those of the forward's
 // per-row pass: slot row_ptr[i] + q for the q-th active edge of row i.
 struct BwdArgs {
-  const float* x;
-  const float* w;
-  const float* sh;            // gate-scaled harmonics per active slot, rows of sh_stride
-  const float* grad_out;
   const float* pos;
   const int32_t* row_ptr;
   const int8_t* shift;
-  const uint8_t* mask;
   const float* gate;
   const int32_t* deg;         // active edges per row
   const int32_t* act_e;       // edge id per active slot
   const int32_t* act_j;       // sender per active slot
-  const PathDev* paths;
-  const int32_t* irrep_start; // paths of input irrep a: irrep_paths[irrep_start[a] .. irrep_start[a+1])
-  const int32_t* irrep_paths;
-  const int32_t* irrep_l;     // per input irrep: l, multiplicity, offset in x
-  const int32_t* irrep_mul;
-  const int32_t* irrep_off;
   const int32_t* t_row_ptr;   // active slots grouped by sender
   const int32_t* t_slot;
   const int32_t* t_recv;
+  const float* part;          // [slot, part_stride] the edge pass's partials
+  const int32_t* xcol_ptr;    // per column c of x: its x-gradient blocks' entries in a row
+  const int32_t* xcol_off;    //   of partials, xcol_off[xcol_ptr[c] .. xcol_ptr[c + 1])
+  const int32_t* ycol_ptr;    // per harmonic component m: its dL/dY entries in a row,
+  const int32_t* ycol_off;    //   ycol_off[ycol_ptr[m] .. ycol_ptr[m + 1])
   float* grad_x;
-  float* grad_w;
-  float* gyp;                 // [slot, gy_stride] per-job dL/dY partials
-  const int2* gy_list;        // per job: {l2, offset of its block in a row of gyp}
-  float* xp;                  // [node, xp_stride] per-path x-gradient partials
   float* grad_r;              // [slot, 3] dL/dr
   float* grad_pos;
-  int32_t n_nodes, n_paths, n_irreps;
-  int32_t f_in, f_out, w_stride, sh_stride, gy_stride, l_sh_max;
-  int32_t want_gy, has_cell, xp_stride, n_gy;
+  int32_t n_nodes, f_in, part_stride, l_sh_max;
+  int32_t want_gy, has_cell;
   double cell[9];
 };
 

@@ -14,98 +14,27 @@
 // hence the gate factor in dL/dr.
 //
 // gfx950 mapping: every pass is deterministic (no floating-point atomics; every sum runs
-// in a fixed order), and each path's coupling is a compile-time specialisation (the real
-// CG coefficients and their sparsity are constants):
-//   * the edge pass (conv_kernel<C, float, true>): the forward's workgroups, producer wave
-//     and schedule, with consumers that write each active edge's w-gradient for their
-//     channels and the job's dL/dY of the edge's slot, reduced over the receiver's lanes
-//     by a fixed butterfly (zero_inactive_kernel clears the rows of inactive edges);
+// in a fixed order):
+//   * the edge pass (conv_kernel_bwd<C>) runs on the forward's workgroups,
+//     producer wave and schedule, each consumer holding its receiver's g; per active
+//     slot it writes the edge's w-gradient, each job's dL/dY of the slot and each job
+//     group's x-gradient of the edge into one row of partials (zero_inactive_kernel
+//     clears the w-gradient rows of inactive edges);
 //   * the active slots are regrouped by sender (counts, scan, placement, per-sender sort
-//     by slot), so that the x-gradient is a gather: on large graphs bwd_x_kernel runs
-//     one wave per (sender, input irrep) and accumulates all of the irrep's paths in
-//     registers; on graphs too small to fill the chip that way bwd_xp_kernel runs one
-//     wave per (sender, path) and writes that path's partial, and bwd_x_sum_kernel adds
-//     each input irrep's partials in path order (either way a path of 32 channels or
-//     fewer puts several of the sender's edges side by side in one wave and adds their
-//     sums by a fixed butterfly);
-//   * bwd_force_kernel evaluates dY/dr by running the harmonics' recurrence on dual
-//     numbers (exact derivatives of the same polynomials), and bwd_pos_kernel sums each
-//     node's +/- contributions in slot order.
+//     by slot); bwd_gather_x_kernel runs one workgroup per sender and column block,
+//     dL/dx[j] being the sum of its slots' x-gradient blocks (rows of partials read in
+//     slot order), and bwd_force_kernel one per sender: each slot's dL/dY (its jobs'
+//     partials in job order) goes through dY/dr, evaluated by running the harmonics'
+//     recurrence on dual numbers (exact derivatives of the same polynomials);
+//   * bwd_pos_kernel sums each node's +/- contributions in slot order.
 #include <hip/hip_runtime.h>
 
 #include "launch.hpp"
 #include "sh_eval.hpp"
-#include "variants.hpp"
 
 namespace cgtp {
 
 namespace {
-
-
-template <int N>
-struct IC {
-  static constexpr int value = N;
-};
-
-template <int B, int E, typename F>
-__device__ __forceinline__ void sfor(F&& f) {
-  if constexpr (B < E) {
-    f(IC<B>{});
-    sfor<B + 1, E>(f);
-  }
-}
-
-template <int L1, int L2, int L3>
-inline constexpr RealCG<L1, L2, L3> kCGb{};
-
-// Runs f(IC<v>) for the variant v of a path: the scalar (K = 1) form of a triple whose
-// largest l is at most LMAX (the kernels here specialise on (l1, l2, l3) only).  Each
-// kernel below is built twice, for l <= 3 and for l = 4 paths, so that the registers
-// the l = 4 code needs do not lower the occupancy of the l <= 3 code.
-constexpr int kBwdLowLmax = 3;
-static_assert(kBwdLmax == kBwdLowLmax + 1, "one high instantiation covers l = kBwdLmax");
-
-template <int LO, int HI, int LMAX, typename F>
-__device__ __forceinline__ void by_variant(int v, F&& f) {
-  if constexpr (HI - LO == 1) {
-    if constexpr (variant_lmax(LO) <= LMAX && variant_desc(LO).k == 1) f(IC<LO>{});
-  } else {
-    constexpr int MID = (LO + HI) / 2;
-    if (v < MID)
-      by_variant<LO, MID, LMAX>(v, f);
-    else
-      by_variant<MID, HI, LMAX>(v, f);
-  }
-}
-
-__device__ __forceinline__ int path_lmax(const PathDev& P) { return max(P.l1, max(P.l2, P.l3)); }
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
-}
-
-__device__ __forceinline__ bool edge_active(const BwdArgs& a, int e) {
-  return (!a.mask || a.mask[e] != 0) && (!a.gate || a.gate[e] != 0.0f);
-}
-
-// A[m1][m3] = sum_m2 C[m1,m2,m3] Y[m2]
-template <int L1, int L2, int L3>
-__device__ __forceinline__ void form_a(const float* Y, float (*A)[2 * L3 + 1]) {
-  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  sfor<0, N1>([&](auto M1) {
-    sfor<0, N3>([&](auto M3) {
-      float s = 0.0f;
-      sfor<0, N2>([&](auto M2) {
-        constexpr float c = kCGb<L1, L2, L3>.at(decltype(M1)::value, decltype(M2)::value, decltype(M3)::value);
-        if constexpr (c != 0.0f) s = __builtin_fmaf(c, Y[decltype(M2)::value], s);
-      });
-      A[decltype(M1)::value][decltype(M3)::value] = s;
-    });
-  });
-}
-
 
 // ---------------------------------------------------------------------------------
 // active slots grouped by sender
@@ -211,204 +140,14 @@ __global__ void __launch_bounds__(kWave) bwd_t_sort_kernel(const int32_t* t_row_
 }
 
 // ---------------------------------------------------------------------------------
-// x-gradient
-// ---------------------------------------------------------------------------------
-
-// entries k0 .. k0 + cnt - 1 of the sender's list: slot, receiver and edge id of entry
-// k0 + lane are held by that lane.  The lanes form nsub sub-groups (sub = this lane's):
-// sub-group g takes entries g, g + nsub, ... (uniform trip count, idle at the tail).
-template <int L1, int L2, int L3>
-__device__ __forceinline__ void bwd_x_path(const BwdArgs& a, const PathDev& P, int cnt, int sub, int nsub,
-                                           int my_s, int my_i, int my_e, int u, bool ok, float* acc) {
-  constexpr int N1 = 2 * L1 + 1, N2 = 2 * L2 + 1, N3 = 2 * L3 + 1;
-  // D-deep pipeline: the harmonics, weight and grad_out rows of the next D entries of
-  // this sub-group are in flight (loaded at clamped indices, unconditionally) while one
-  // entry is used; D from the registers an entry holds
-  struct Entry {
-    float Y[N2];
-    float w;
-    float go[N3];
-  };
-  constexpr int D = 48 / (N2 + 1 + N3) < 2 ? 2 : (48 / (N2 + 1 + N3) > 4 ? 4 : 48 / (N2 + 1 + N3));
-  const int uu = ok ? u : 0;
-  auto load = [&](int k, Entry& d) {
-    const int s = __shfl(my_s, k, kWave), i = __shfl(my_i, k, kWave), e = __shfl(my_e, k, kWave);
-#pragma unroll
-    for (int m = 0; m < N2; ++m) d.Y[m] = a.sh[(long)s * a.sh_stride + P.sh_off + m];
-    d.w = a.w[(long)e * a.w_stride + P.w_off + uu];
-#pragma unroll
-    for (int m = 0; m < N3; ++m) d.go[m] = a.grad_out[(long)i * a.f_out + P.out_off + uu * N3 + m];
-  };
-  const int steps = (cnt + nsub - 1) / nsub;
-  Entry ring[D];
-#pragma unroll
-  for (int r = 0; r < D; ++r) load(min(sub + r * nsub, cnt - 1), ring[r]);
-  for (int t0 = 0; t0 < steps; t0 += D) {
-#pragma unroll
-    for (int r = 0; r < D; ++r) {
-      const int t = t0 + r;
-      if (t < steps) {   // uniform over the wave
-        const int k = t * nsub + sub;
-        const Entry cur = ring[r];
-        load(min(k + D * nsub, cnt - 1), ring[r]);
-        float A[N1][N3];
-        form_a<L1, L2, L3>(cur.Y, A);
-        if (ok && k < cnt) {
-#pragma unroll
-          for (int m1 = 0; m1 < N1; ++m1) {
-            float v = 0.0f;
-#pragma unroll
-            for (int m3 = 0; m3 < N3; ++m3) v = __builtin_fmaf(A[m1][m3], cur.go[m3], v);
-            acc[m1] = __builtin_fmaf(cur.w, v, acc[m1]);
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int L1, int LMAX>
-__device__ __forceinline__ void bwd_x_irrep(const BwdArgs& a, int j, int ir) {
-  constexpr int N1 = 2 * L1 + 1;
-  const int mul = a.irrep_mul[ir], off = a.irrep_off[ir];
-  const int p0 = a.irrep_start[ir], p1 = a.irrep_start[ir + 1];
-  // lanes per entry: the next power of two of the multiplicity, at most 64; the
-  // 64 / cw sub-groups of a wave walk interleaved entries of the sender's list and their
-  // partial sums are added by a fixed butterfly before the store
-  int cw = 1;
-  while (cw < mul && cw < kWave) cw <<= 1;
-  const int lane = int(threadIdx.x), sub = lane / cw, nsub = kWave / cw;
-  for (int u0 = 0; u0 < mul; u0 += kWave) {
-    const int u = u0 + (lane & (cw - 1));
-    const bool ok = u < mul;
-    float acc[N1];
-#pragma unroll
-    for (int m = 0; m < N1; ++m) acc[m] = 0.0f;
-    const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
-    for (int k0 = tb; k0 < te; k0 += kWave) {
-      const int cnt = min(kWave, te - k0);
-      const int kk = k0 + min(int(threadIdx.x), cnt - 1);
-      const int my_s = a.t_slot[kk], my_i = a.t_recv[kk];
-      const int my_e = a.act_e[my_s];
-      for (int pp = p0; pp < p1; ++pp) {
-        const PathDev P = a.paths[a.irrep_paths[pp]];
-        by_variant<0, kNumVariants, LMAX>(P.variant, [&](auto V) {
-          constexpr VariantDesc d = variant_desc(decltype(V)::value);
-          if constexpr (d.l1 == L1) bwd_x_path<L1, d.l2, d.l3>(a, P, cnt, sub, nsub, my_s, my_i, my_e, u, ok, acc);
-        });
-      }
-    }
-    for (int d = cw; d < kWave; d <<= 1) {
-#pragma unroll
-      for (int m = 0; m < N1; ++m) acc[m] += __shfl_xor(acc[m], d, kWave);
-    }
-    if (ok && sub == 0) {
-#pragma unroll
-      for (int m = 0; m < N1; ++m) a.grad_x[(long)j * a.f_in + off + u * N1 + m] = acc[m];
-    }
-  }
-}
-
-// One wave per (sender, input irrep), all of the irrep's paths accumulated in registers
-// and stored once (no partials).  HIGH: the instantiation for the input irreps with a
-// path of l = kBwdLmax.
-template <bool HIGH>
-__global__ void __launch_bounds__(kWave) bwd_x_kernel(BwdArgs a) {
-  const int j = int(blockIdx.x), ir = int(blockIdx.y);
-  int lm = 0;
-  for (int pp = a.irrep_start[ir]; pp < a.irrep_start[ir + 1]; ++pp) lm = max(lm, path_lmax(a.paths[a.irrep_paths[pp]]));
-  if ((lm > kBwdLowLmax) != HIGH) return;
-  constexpr int LM = HIGH ? kBwdLmax : kBwdLowLmax;
-  switch (a.irrep_l[ir]) {
-    case 0: bwd_x_irrep<0, LM>(a, j, ir); break;
-    case 1: bwd_x_irrep<1, LM>(a, j, ir); break;
-    case 2: bwd_x_irrep<2, LM>(a, j, ir); break;
-    case 3: bwd_x_irrep<3, LM>(a, j, ir); break;
-    case 4:
-      if constexpr (HIGH) bwd_x_irrep<4, LM>(a, j, ir);
-      break;
-    default: break;
-  }
-}
-
-// One wave per (sender, path): the path's x-gradient partial of every channel of the
-// sender, over its entries in slot order, written to the path's block of the sender's
-// row of partials.  A path of 32 channels or fewer runs 64 / 2^ceil(log2 mul) of the
-// sender's entries side by side and adds the sub-groups' sums by a fixed butterfly.
-template <bool HIGH>
-__global__ void __launch_bounds__(kWave) bwd_xp_kernel(BwdArgs a) {
-  const int j = int(blockIdx.x);
-  const PathDev P = a.paths[blockIdx.y];
-  if ((path_lmax(P) > kBwdLowLmax) != HIGH) return;
-  int cw = 1;
-  while (cw < P.mul && cw < kWave) cw <<= 1;
-  const int lane = int(threadIdx.x), sub = lane / cw, nsub = kWave / cw;
-  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
-  by_variant<0, kNumVariants, HIGH ? kBwdLmax : kBwdLowLmax>(P.variant, [&](auto V) {
-    constexpr VariantDesc d = variant_desc(decltype(V)::value);
-    constexpr int N1 = 2 * d.l1 + 1;
-    for (int u0 = 0; u0 < P.mul; u0 += kWave) {
-      const int u = u0 + (lane & (cw - 1));
-      const bool ok = u < P.mul;
-      float acc[N1];
-#pragma unroll
-      for (int m = 0; m < N1; ++m) acc[m] = 0.0f;
-      for (int k0 = tb; k0 < te; k0 += kWave) {
-        const int cnt = min(kWave, te - k0);
-        const int kk = k0 + min(lane, cnt - 1);
-        const int my_s = a.t_slot[kk], my_i = a.t_recv[kk];
-        const int my_e = a.act_e[my_s];
-        bwd_x_path<d.l1, d.l2, d.l3>(a, P, cnt, sub, nsub, my_s, my_i, my_e, u, ok, acc);
-      }
-      for (int dd = cw; dd < kWave; dd <<= 1) {
-#pragma unroll
-        for (int m = 0; m < N1; ++m) acc[m] += __shfl_xor(acc[m], dd, kWave);
-      }
-      if (ok && sub == 0) {
-#pragma unroll
-        for (int m = 0; m < N1; ++m) a.xp[(long)j * a.xp_stride + P.xp_off + u * N1 + m] = acc[m];
-      }
-    }
-  });
-}
-
-// x-gradient: per node and input-feature column, the partials of the column's irrep's
-// paths added in path order (an irrep without paths gets 0)
-__global__ void __launch_bounds__(256) bwd_x_sum_kernel(BwdArgs a) {
-  const long idx = long(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= long(a.n_nodes) * a.f_in) return;
-  const int j = int(idx / a.f_in), c = int(idx - long(j) * a.f_in);
-  int ir = 0;
-  while (ir + 1 < a.n_irreps && a.irrep_off[ir + 1] <= c) ++ir;
-  const int r = c - a.irrep_off[ir];
-  float v = 0.0f;
-  for (int pp = a.irrep_start[ir]; pp < a.irrep_start[ir + 1]; ++pp)
-    v += a.xp[(long)j * a.xp_stride + a.paths[a.irrep_paths[pp]].xp_off + r];
-  a.grad_x[idx] = v;
-}
-
-// ---------------------------------------------------------------------------------
 // dL/dr per active slot, and the position gradient
 // ---------------------------------------------------------------------------------
 
+// dL/dr of active slot s (edge j -> i) from its dL/dY, g[0 .. (L + 1)^2)
 template <int L>
-__device__ __forceinline__ void slot_grad_r(const BwdArgs& a, int i, int s) {
+__device__ __forceinline__ void slot_grad_r(const BwdArgs& a, int i, int j, int s, const float* g) {
   constexpr int NY = (L + 1) * (L + 1);
-  // dL/dY of the slot: the jobs' partials (one per path and channel block) in job order
-  float g[NY];
-#pragma unroll
-  for (int k = 0; k < NY; ++k) g[k] = 0.0f;
-  for (int q = 0; q < a.n_gy; ++q) {
-    const int2 jb = a.gy_list[q];   // {l2, offset in a row of partials}
-    sfor<1, L + 1>([&](auto L2c) {
-      constexpr int L2 = decltype(L2c)::value;
-      if (jb.x == L2) {
-#pragma unroll
-        for (int m = 0; m < 2 * L2 + 1; ++m) g[L2 * L2 + m] += a.gyp[(long)s * a.gy_stride + jb.y + m];
-      }
-    });
-  }
-  const int e = a.act_e[s], j = a.act_j[s];
+  const int e = a.act_e[s];
   double r[3];
 #pragma unroll
   for (int k = 0; k < 3; ++k) r[k] = double(a.pos[3 * j + k]) - double(a.pos[3 * i + k]);
@@ -444,22 +183,126 @@ __device__ __forceinline__ void slot_grad_r(const BwdArgs& a, int i, int s) {
   for (int k = 0; k < 3; ++k) a.grad_r[(long)s * 3 + k] = float(gr[k]);
 }
 
-// one wave per row, lanes over its active slots
-__global__ void __launch_bounds__(256) bwd_force_kernel(BwdArgs a) {
-  const int i = int(blockIdx.x) * (256 / kWave) + int(threadIdx.x) / kWave;
-  if (i >= a.n_nodes) return;
-  const int lane = int(threadIdx.x) & (kWave - 1);
-  const int rb = a.row_ptr[i], d = a.deg[i];
-  for (int q = lane; q < d; q += kWave) {
-    switch (a.l_sh_max) {
-      case 1: slot_grad_r<1>(a, i, rb + q); break;
-      case 2: slot_grad_r<2>(a, i, rb + q); break;
-      case 3: slot_grad_r<3>(a, i, rb + q); break;
-      case 4: slot_grad_r<4>(a, i, rb + q); break;
-      default:   // l = 0 harmonics only: constant, no gradient
+// One workgroup per (sender j, block of kGatherThreads columns of x).  dL/dx[j, c] is
+// the sum over j's active slots, in slot order, of the entries of column c in the slot's
+// row of partials (the x-gradient blocks of the groups that read c, in group order).
+// The sender's slots are staged in LDS by chunks and each thread keeps its column's
+// entry offsets in registers, so that the loads of several slots are in flight at once.
+constexpr int kGatherThreads = 256;
+constexpr int kMaxCover = 4;   // x-gradient blocks per column held in registers
+constexpr int kGatherBatch = 4;   // slots whose loads are issued together
+
+// acc + the column's entries of the n staged slots, NQ entries per slot loaded for every
+// lane (lanes with fewer, nq, repeat a valid offset and drop the extra values): all
+// loads of a batch are unconditional, so they are in flight together
+template <int NQ>
+__device__ __forceinline__ float gather_cols(const BwdArgs& a, const int* ss, int n, const int* off, int nq,
+                                             float acc) {
+  for (int t = 0; t < n; t += kGatherBatch) {
+    float v[kGatherBatch][NQ];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) a.grad_r[(long)(rb + q) * 3 + k] = 0.0f;
+    for (int u = 0; u < kGatherBatch; ++u) {
+      const float* row = a.part + (long)ss[t + u < n ? t + u : t] * a.part_stride;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) v[u][q] = row[off[q]];
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherBatch; ++u)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) acc = (t + u < n && q < nq) ? acc + v[u][q] : acc;
+  }
+  return acc;
+}
+
+__global__ void __launch_bounds__(kGatherThreads) bwd_gather_x_kernel(BwdArgs a) {
+  __shared__ int ss[kGatherThreads];
+  const int j = int(blockIdx.x);
+  const int tid = int(threadIdx.x);
+  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
+  const int c = int(blockIdx.y) * kGatherThreads + tid;
+  const bool col_ok = c < a.f_in;
+  int q0 = 0, nq = 0;
+  if (col_ok) {
+    q0 = a.xcol_ptr[c];
+    nq = a.xcol_ptr[c + 1] - q0;
+  }
+  int off[kMaxCover];
+#pragma unroll
+  for (int q = 0; q < kMaxCover; ++q) off[q] = nq > 0 ? a.xcol_off[q0 + (q < nq ? q : 0)] : 0;
+  // the wave's largest cover selects the unrolled form (uniform)
+  int nqw = nq;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) nqw = max(nqw, __shfl_xor(nqw, o, kWave));
+  nqw = __builtin_amdgcn_readfirstlane(nqw);
+  float acc = 0.0f;
+  for (int t0 = tb; t0 < te; t0 += kGatherThreads) {
+    const int n = min(kGatherThreads, te - t0);
+    __syncthreads();   // the previous chunk is consumed
+    if (tid < n) ss[tid] = a.t_slot[t0 + tid];
+    __syncthreads();
+    switch (nqw) {
+      case 0: break;
+      case 1: acc = gather_cols<1>(a, ss, n, off, nq, acc); break;
+      case 2: acc = gather_cols<2>(a, ss, n, off, nq, acc); break;
+      case 3: acc = gather_cols<3>(a, ss, n, off, nq, acc); break;
+      case 4: acc = gather_cols<4>(a, ss, n, off, nq, acc); break;
+      default:
+        if (col_ok)
+          for (int t = 0; t < n; ++t) {
+            const float* row = a.part + (long)ss[t] * a.part_stride;
+            for (int q = 0; q < nq; ++q) acc += row[a.xcol_off[q0 + q]];
+          }
         break;
+    }
+  }
+  if (col_ok) a.grad_x[(long)j * a.f_in + c] = acc;
+}
+
+// One workgroup per sender j: dL/dr of its active slots.  Per chunk of kForceSlots slots,
+// their dL/dY (each harmonic component's job partials, in job order, read from the
+// slots' rows of partials) is summed into LDS, then one thread per slot evaluates dL/dr.
+constexpr int kForceThreads = 256;
+constexpr int kForceSlots = 16;
+constexpr int kMaxGyLen = 1024;   // dL/dY entries of a row whose offsets are staged in LDS
+
+template <int L>
+__global__ void __launch_bounds__(kForceThreads) bwd_force_kernel(BwdArgs a) {
+  const int j = int(blockIdx.x);
+  const int tid = int(threadIdx.x);
+  const int tb = a.t_row_ptr[j], te = a.t_row_ptr[j + 1];
+  if constexpr (L == 0) {   // l = 0 harmonics only: constant, no gradient
+    for (int t = tb + tid; t < te; t += kForceThreads)
+#pragma unroll
+      for (int k = 0; k < 3; ++k) a.grad_r[(long)a.t_slot[t] * 3 + k] = 0.0f;
+  } else {
+    constexpr int NY = (L + 1) * (L + 1);
+    __shared__ float gys[kForceSlots][NY];
+    __shared__ int yoff[kMaxGyLen];
+    __shared__ int yptr[NY + 1];
+    if (tb == te) return;
+    const int ny_len = a.ycol_ptr[NY];
+    const bool staged = ny_len <= kMaxGyLen;
+    if (tid <= NY) yptr[tid] = a.ycol_ptr[tid];
+    if (staged)
+      for (int q = tid; q < ny_len; q += kForceThreads) yoff[q] = a.ycol_off[q];
+    __syncthreads();
+    for (int t0 = tb; t0 < te; t0 += kForceSlots) {
+      const int n = min(kForceSlots, te - t0);
+      for (int idx = tid; idx < n * NY; idx += kForceThreads) {
+        const int r = idx / NY, m = idx - r * NY;
+        const float* row = a.part + (long)a.t_slot[t0 + r] * a.part_stride;
+        float v = 0.0f;
+        if (staged) {
+#pragma unroll 4
+          for (int q = yptr[m]; q < yptr[m + 1]; ++q) v += row[yoff[q]];
+        } else {
+          for (int q = yptr[m]; q < yptr[m + 1]; ++q) v += row[a.ycol_off[q]];
+        }
+        gys[r][m] = v;
+      }
+      __syncthreads();
+      if (tid < n) slot_grad_r<L>(a, a.t_recv[t0 + tid], j, a.t_slot[t0 + tid], gys[tid]);
+      __syncthreads();
     }
   }
 }
@@ -511,30 +354,29 @@ hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s) {
-  if (a.n_nodes == 0 || a.n_irreps == 0) return hipSuccess;
-  // With enough (sender, irrep) waves to fill the chip (4 per SIMD) each wave takes a
-  // whole irrep; otherwise one wave per (sender, path) and a fixed-order sum, which
-  // shortens each wave's chain of dependent loads at the price of the partials' traffic.
-  constexpr long kFillWaves = 4L * 1024;
-  if (long(a.n_nodes) * a.n_irreps >= kFillWaves) {
-    bwd_x_kernel<false><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
-    if (high) bwd_x_kernel<true><<<dim3(a.n_nodes, a.n_irreps), kWave, 0, s>>>(a);
-    return hipGetLastError();
+hipError_t launch_bwd_gather_x(const BwdArgs& a, hipStream_t s) {
+  if (a.n_nodes == 0 || a.f_in == 0) return hipSuccess;
+  bwd_gather_x_kernel<<<dim3(a.n_nodes, ceil_div(a.f_in, kGatherThreads)), kGatherThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_force(const BwdArgs& a, hipStream_t s) {
+  const int n = a.n_nodes;
+  if (n == 0) return hipSuccess;
+  switch (a.l_sh_max) {
+    case 0: bwd_force_kernel<0><<<n, kForceThreads, 0, s>>>(a); break;
+    case 1: bwd_force_kernel<1><<<n, kForceThreads, 0, s>>>(a); break;
+    case 2: bwd_force_kernel<2><<<n, kForceThreads, 0, s>>>(a); break;
+    case 3: bwd_force_kernel<3><<<n, kForceThreads, 0, s>>>(a); break;
+    case 4: bwd_force_kernel<4><<<n, kForceThreads, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
   }
-  if (a.n_paths > 0) {
-    bwd_xp_kernel<false><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
-    if (high) bwd_xp_kernel<true><<<dim3(a.n_nodes, a.n_paths), kWave, 0, s>>>(a);
-  }
-  const long total = long(a.n_nodes) * a.f_in;
-  bwd_x_sum_kernel<<<int((total + 255) / 256), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s) {
   const int n = a.n_nodes;
   if (n == 0) return hipSuccess;
-  bwd_force_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
   bwd_pos_kernel<<<ceil_div(n, 256 / kWave), 256, 0, s>>>(a);
   return hipGetLastError();
 }

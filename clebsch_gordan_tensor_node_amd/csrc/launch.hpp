@@ -59,9 +59,10 @@ hipError_t launch_compact(const int32_t* row_ptr, const uint8_t* mask, const int
 // ev_start / ev_stop (may be null): HIP events stamped at this launch's start / end.
 template <int C, typename T>
 hipError_t launch_conv_class(const ConvArgsT<T>& args, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop);
-// The backward's edge pass over the same launch (args.grad_out, grad_w (may be null),
-// gyp, job_gy, scratch_row set): the w-gradient of every active edge and the per-job
-// dL/dY of every active slot.  Classes 0 .. kNumClassesBwd - 1.
+// The backward's edge pass over the same launch (args.grad_out, scratch_row, job_gy,
+// job_xg and part_stride set; grad_w, gyp and xgp each null to skip): the w-gradient of
+// every active edge and, per active slot, a row of partials holding each job's dL/dY and
+// each job group's x-gradient of the edge.  Classes 0 .. kNumClassesBwd - 1.
 template <int C>
 hipError_t launch_conv_bwd_class(const ConvArgsT<float>& args, hipStream_t s);
 hipError_t launch_conv_bwd(const ConvArgsT<float>& args, int cls, hipStream_t s);
@@ -82,11 +83,11 @@ constexpr int kBwdLmax = 4;
 // sender's entries in slot order.  t_cnt: [n] scratch.
 hipError_t launch_bwd_transpose(const BwdArgs& a, int32_t* t_cnt, int32_t* t_row_ptr, int32_t* t_slot,
                                 int32_t* t_recv, hipStream_t s);
-// x-gradient: one wave per (sender, input irrep) when those waves fill the chip, else
-// per-path partials (one wave per (sender, path)) and their sum per input irrep in path
-// order; high as for the edge pass (the l = kBwdLmax paths run in a second launch).
-hipError_t launch_bwd_x(const BwdArgs& a, bool high, hipStream_t s);
-// dL/dr per active slot from the partials and dY/dr, then the position gradient.
+// Per sender: dL/dx from the edge pass's x-gradient blocks of its slots.
+hipError_t launch_bwd_gather_x(const BwdArgs& a, hipStream_t s);
+// Per sender: dL/dr of its slots from their dL/dY partials and dY/dr.
+hipError_t launch_bwd_force(const BwdArgs& a, hipStream_t s);
+// The position gradient from dL/dr: + at each slot's sender, - at its receiver.
 hipError_t launch_bwd_pos(const BwdArgs& a, hipStream_t s);
 
 }  // namespace cgtp
