@@ -94,22 +94,27 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
                      int path_rule, unsigned flags, cgtp_plan_t* out);
 
 /* Sizes of the plan.  Any output pointer may be NULL.  irreps_out receives the
- * output irreps string (NUL-terminated, truncated to irreps_out_cap). */
+ * output irreps string (NUL-terminated, truncated to irreps_out_cap); for the six
+ * irreps cases of LunaTP Table 1 it is the output column of that table. */
 int cgtp_plan_info(cgtp_plan_t plan, int64_t* f_in, int64_t* f_out, int64_t* w_per_edge,
                    int* n_paths, int* l_sh_max, char* irreps_out, size_t irreps_out_cap);
 
 /* Host array rows[n_paths * 10]: l1, p1, l2, p2, l3, p3, mul, in_off, out_off, w_off
- * per path (offsets as in the layouts above). */
+ * per path (offsets as in the layouts above): the uvu paths whose outputs make up the
+ * output irreps of LunaTP Table 1. */
 int cgtp_plan_paths(cgtp_plan_t plan, int32_t* rows);
 
 /* Host array dense[(2l1+1)(2l2+1)(2l3+1)] = real CG of path `path`, fp32, index
- * ((m1+l1)(2l2+1) + (m2+l2))(2l3+1) + (m3+l3). */
+ * ((m1+l1)(2l2+1) + (m2+l2))(2l3+1) + (m3+l3): the sparse coupling coefficients that
+ * LunaTP Figure 3(c) treats as constants of the kernel. */
 int cgtp_plan_cg(cgtp_plan_t plan, int path, float* dense);
 
 /* Scheduler summary: number of wave jobs and of distinct kernel variants used. */
 int cgtp_plan_schedule(cgtp_plan_t plan, int* n_jobs, int* n_variants);
 
-/* Workspace bytes that cgtp_conv_forward needs for this graph size (alignment 256). */
+/* Workspace bytes that cgtp_conv_forward needs for this graph size (alignment 256).
+ * Interface bookkeeping: the pages define no such call; it exists because the library
+ * allocates nothing. */
 int cgtp_workspace_size(cgtp_plan_t plan, int64_t n_nodes, int64_t n_edges, int has_mask,
                         size_t* bytes);
 
@@ -255,9 +260,12 @@ int cgtp_conv_backward(cgtp_plan_t plan, const float* pos, int64_t n_nodes, cons
                        const float* gate, const float* grad_out, float* grad_x, float* grad_w,
                        float* grad_pos, void* workspace, size_t ws_bytes, void* stream);
 
+/* Frees the plan's device tables, streams and events (interface bookkeeping; the pages
+ * define no such call).  NULL is ignored. */
 void cgtp_plan_destroy(cgtp_plan_t plan);
 
-/* Thread-local message of the last failing call ("" if none). */
+/* Thread-local message of the last failing call ("" if none).  Interface bookkeeping;
+ * the pages define no such call. */
 const char* cgtp_last_error(void);
 
 /* Library version string. */
