@@ -190,6 +190,7 @@ struct GroupLoad {
 // l <= 3, c2_768 56.2 against 51.3 us and si_mask 108.3 against 105.0 us.
 struct Schedule {
   int jobs_per_group[kNumClasses] = {};
+  bool balance_simds = false;        // jobs of a group placed for SIMD balance (the forward)
   std::vector<Job> jobs;             // ordered by group
   std::vector<Group> groups;         // by kernel class, heavy groups first
   std::vector<int> class_begin;      // [kNumClasses + 1] first group of each class
@@ -243,8 +244,8 @@ namespace {
 // class, input irrep, channel block and K form a set that shares x_j rows; each set is
 // cut into groups of at most S.jobs_per_group[class] jobs, one workgroup per group and
 // node group.
-// Jobs keep their weight-column order inside a set, so that a group's consumers read
-// adjacent columns of each weight row; groups are ordered heaviest first inside a class
+// Jobs keep their weight-column order inside a set (the forward's schedule then places
+// a group's jobs on waves for SIMD balance, below); groups are ordered heaviest first inside a class
 // (LunaTP Table 9: ordering by descending CG-term count was fastest).
 void schedule(const cgtp_plan_s& P, Schedule& S) {
   S.jobs.clear();
@@ -341,6 +342,7 @@ void schedule(const cgtp_plan_s& P, Schedule& S) {
   S.groups.clear();
   S.group_load.clear();
   S.class_begin.assign(kNumClasses + 1, 0);
+  std::vector<double> jcost;   // per job of S.jobs: its lane's work per edge step
   for (const G& g : gs) {
     Group G{};
     G.first_job = int(S.jobs.size());
@@ -349,6 +351,7 @@ void schedule(const cgtp_plan_s& P, Schedule& S) {
     int l2lo = kMaxL, l2hi = 0;
     for (int k = g.begin; k < g.begin + g.n; ++k) {
       S.jobs.push_back(tmp[k].j);
+      jcost.push_back(tmp[k].cost);
       l2lo = std::min(l2lo, tmp[k].l2);
       l2hi = std::max(l2hi, tmp[k].l2);
     }
@@ -385,6 +388,52 @@ void schedule(const cgtp_plan_s& P, Schedule& S) {
     int most = 1;
     for (int k = L.g0; k < L.g1; ++k) most = std::max(most, S.groups[k].n_jobs);
     L.waves = most + 1;
+  }
+  // SIMD balance.  A CU deals the waves of a workgroup to its four SIMDs in turn, so
+  // waves w and w + 4 share a SIMD, and the producer (the last wave) shares one with a
+  // consumer; every wave meets the others at each step's barrier, so a step lasts as
+  // long as the busiest SIMD's waves.  The jobs of a group are placed heaviest first on
+  // the least loaded SIMD that still has a consumer position (conv kernel time against
+  // weight-column order: si_mask 104.9 -> 103.2 us, c5_768 147.5 -> 144.7, c2_768
+  // 51.8 -> 51.5).  Only the forward's schedule is rearranged: the backward's tables
+  // follow its own job order.
+  if (S.balance_simds) {
+    constexpr double kStepOverhead = 25.0;   // LDS reads, weight select and addressing
+    for (const ConvLaunch& L : S.launches) {
+      for (int k = L.g0; k < L.g1; ++k) {
+        const Group& G = S.groups[k];
+        if (G.n_jobs < 2 || L.waves <= 4) continue;
+        const int n = G.n_jobs;
+        const int l1 = variant_desc(S.jobs[G.first_job].variant).l1;
+        double load[4] = {};
+        load[(L.waves - 1) % 4] += 4.0 * (2 * l1 + 2);   // the producer's loads and stores
+        std::vector<int> ord(n);
+        for (int q = 0; q < n; ++q) ord[q] = q;
+        std::stable_sort(ord.begin(), ord.end(), [&](int a, int b) {
+          return jcost[G.first_job + a] > jcost[G.first_job + b];
+        });
+        std::vector<int> pos_of(n, -1);
+        std::vector<char> used(n, 0);
+        for (int q : ord) {
+          int best = -1;
+          for (int p = 0; p < n; ++p)
+            if (!used[p] && (best < 0 || load[p % 4] < load[best % 4])) best = p;
+          used[best] = 1;
+          pos_of[q] = best;
+          load[best % 4] += jcost[G.first_job + q] + kStepOverhead;
+        }
+        std::vector<Job> js(n);
+        std::vector<double> cs(n);
+        for (int q = 0; q < n; ++q) {
+          js[pos_of[q]] = S.jobs[G.first_job + q];
+          cs[pos_of[q]] = jcost[G.first_job + q];
+        }
+        for (int q = 0; q < n; ++q) {
+          S.jobs[G.first_job + q] = js[q];
+          jcost[G.first_job + q] = cs[q];
+        }
+      }
+    }
   }
   std::vector<double> est(S.launches.size(), 0.0);
   for (size_t li = 0; li < S.launches.size(); ++li) {
@@ -584,6 +633,7 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
     P->fwd.jobs_per_group[c] = c == 1 ? kConvJobsFwd : kConvJobsBwd;
     P->bwd.jobs_per_group[c] = kConvJobsBwd;
   }
+  P->fwd.balance_simds = true;
   schedule(*P, P->fwd);
   schedule(*P, P->bwd);
   // backward tables
