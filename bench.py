@@ -18,8 +18,9 @@ bandwidth target); the `configs` block repeats the same measurement for the othe
 Timing is MALL-honest: the weights (and outputs) rotate over enough distinct buffers
 (>= 768 MB in total) that the 256 MB last-level cache cannot hold them between the
 steps that reuse them; the warm-cache time (one buffer) is reported as an extra field.
-Three timed passes of K steps each: (A) nothing but the steps in the stream, which
-gives ms_per_step and the throughput; (B) every step bracketed by its own events, which
+Three kinds of timed passes of K steps each: (A) nothing but the steps in the stream,
+run PASSES_A times, the least of which gives ms_per_step and the throughput (all are
+reported); (B) every step bracketed by its own events, which
 gives the per-step p10 / p50 / p90; (C) the library stamps every fused convolution
 launch with dispatch events on the same stream, which times the dominant kernel live
 (the stamps add gaps around the launch, so they stay out of pass A).
@@ -53,6 +54,11 @@ KERNEL_SOURCES = ["conv_kernel.hpp", "cg_real.hpp", "common.hpp", "variants.hpp"
 HEADLINE = "si_mask"
 CONFIGS = "c1_768,c2_768,highl_768,si_mask"
 HOST_THREADS_CAP = 16               # CPU share of one GPU on the measurement hosts
+# Timed passes of K steps behind ms_per_step (the least of them is reported, every one
+# beside it): on the measurement boxes a whole pass of a few tens of milliseconds now and
+# then runs up to 2.5 times slower than the passes around it, with the kernels and the
+# host enqueue (about 20 us a step, a sixth of the GPU's time) unchanged.
+PASSES_A = 3
 
 
 def kernel_hash() -> str:
@@ -217,6 +223,24 @@ def _pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
 
+def timed_passes(step, first, K, passes=None):
+    """PASSES_A timed passes of K steps each (step indices from `first` on), each
+    bracketed by synchronisations and timed by a pair of events around the K steps;
+    returns the milliseconds per step of each pass."""
+    import torch
+    out = []
+    for p in range(passes or PASSES_A):
+        torch.cuda.synchronize()
+        b, t = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b.record()
+        for s in range(K):
+            step(first + p * K + s)
+        t.record()
+        torch.cuda.synchronize()
+        out.append(b.elapsed_time(t) / K)
+    return out
+
+
 def measure_forward(C, wl, dev, K, W, f64=False, warm_cache=True):
     """Passes A, B and C (module docstring) over one workload; returns a dict."""
     import numpy as np
@@ -272,41 +296,32 @@ def measure_forward(C, wl, dev, K, W, f64=False, warm_cache=True):
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    # A: throughput, K whole steps with nothing else in the stream
-    t_beg, t_end = ev(), ev()
-    t_beg.record()
-    for s in range(K):
-        step(W + s)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_beg.elapsed_time(t_end) / K
+    # A: throughput, K whole steps with nothing else in the stream, PASSES_A times
+    passes = timed_passes(step, W, K)
+    ms_step = min(passes)
     # B: per-step distribution
     for s in range(K):
         st_b[s].record()
-        step(W + K + s)
+        step(W + PASSES_A * K + s)
         st_e[s].record()
     torch.cuda.synchronize()
     steps_ms = [st_b[s].elapsed_time(st_e[s]) for s in range(K)]
     # C: the convolution launches, stamped by dispatch events
     for s in range(K):
-        step(W + 2 * K + s, (ev_b[s], ev_e[s]))
+        step(W + (PASSES_A + 1) * K + s, (ev_b[s], ev_e[s]))
     torch.cuda.synchronize()
     conv = [ev_b[s].elapsed_time(ev_e[s]) for s in range(K)]
     conv_ms = float(np.mean(conv))
     ms_warm = None
     if warm_cache:   # one weight buffer reused every step
-        t_beg.record()
-        for s in range(K):
-            C.conv_forward(plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs[0], mask_d, out=outs[0],
-                           workspace=ws, gate=gate_d)
-        t_end.record()
-        torch.cuda.synchronize()
-        ms_warm = t_beg.elapsed_time(t_end) / K
+        ms_warm = min(timed_passes(lambda s: C.conv_forward(plan, pos_d, cell, row_ptr, col, shift, x_d, wbufs[0],
+                                                            mask_d, out=outs[0], workspace=ws, gate=gate_d),
+                                   0, K, passes=2))
     nbytes = alg_bytes(plan, n, e, e_act, elem, mask is not None, gate is not None)
     flops = alg_flops_per_edge(plan) * e_act
     res = {
         "plan": plan, "n": n, "e": e, "e_act": e_act, "k": k,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "ms_per_step_passes": passes,
         "ms_per_step_p10": _pct(steps_ms, 10), "ms_per_step_p50": _pct(steps_ms, 50),
         "ms_per_step_p90": _pct(steps_ms, 90),
         "conv_ms": conv_ms, "conv_ms_p10": _pct(conv, 10), "conv_ms_p50": _pct(conv, 50),
@@ -514,13 +529,8 @@ def bench_backward(a, C, wl, dev):
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
-    t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_beg.record()
-    for s in range(K):
-        step(W + s)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_beg.elapsed_time(t_end) / K
+    passes = timed_passes(step, W, K)
+    ms_step = min(passes)
     # algorithmic bytes of the backward, each moved once: w of the active edges and the
     # w-gradient of every edge (4 W each), the edge list (as the forward), x and
     # grad_x (4 F_in per node each), grad_out (4 F_out per node), positions and their
@@ -537,6 +547,7 @@ def bench_backward(a, C, wl, dev):
         "steps": K,
         "warmup": W,
         "ms_per_step": ms_step,
+        "ms_per_step_passes": passes,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -190,7 +190,13 @@ __device__ __forceinline__ void slot_grad_r(const BwdArgs& a, int i, int j, int 
 // entry offsets in registers, so that the loads of several slots are in flight at once.
 constexpr int kGatherThreads = 256;
 constexpr int kMaxCover = 4;   // x-gradient blocks per column held in registers
-constexpr int kGatherBatch = 4;   // slots whose loads are issued together
+// slots whose loads are issued together: a sender's whole slot list at the common
+// degrees (one memory latency per workgroup instead of one per four slots), in as
+// many registers as NQ entries allow
+template <int NQ>
+constexpr int gather_batch() {
+  return NQ <= 2 ? 16 : 8;
+}
 
 // acc + the column's entries of the n staged slots, NQ entries per slot loaded for every
 // lane (lanes with fewer, nq, repeat a valid offset and drop the extra values): all
@@ -198,6 +204,7 @@ constexpr int kGatherBatch = 4;   // slots whose loads are issued together
 template <int NQ>
 __device__ __forceinline__ float gather_cols(const BwdArgs& a, const int* ss, int n, const int* off, int nq,
                                              float acc) {
+  constexpr int kGatherBatch = gather_batch<NQ>();
   for (int t = 0; t < n; t += kGatherBatch) {
     float v[kGatherBatch][NQ];
 #pragma unroll
