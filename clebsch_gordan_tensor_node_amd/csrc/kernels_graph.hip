@@ -485,16 +485,47 @@ __global__ void __launch_bounds__(kScanThreads) prep_scan_order_kernel(const int
 
 constexpr int kOrderBins = kScanThreads;
 
+// Graphs of up to kOrderCache nodes keep each node's degree and row start in LDS from
+// the counting pass to the placing pass, which then reads no global memory (one memory
+// round trip per launch instead of two); every load of the counting pass is issued before
+// the first is used.
+constexpr int kOrderCache = 6144;
+constexpr int kOrderUnroll = (kOrderCache + kScanThreads - 1) / kScanThreads;
+
 // deg may be null: then every edge is active and deg[i] = row_ptr[i + 1] - row_ptr[i]
 __device__ inline void degree_order_body(const int32_t* __restrict__ deg, int n, const int32_t* __restrict__ row_ptr,
                                          int4* __restrict__ node_info) {
   __shared__ int wsum[kScanWaves + 1];
   __shared__ int cursor[kOrderBins];
+  __shared__ int c_deg[kOrderCache];
+  __shared__ int c_row[kOrderCache];
+  if (n <= 0) return;   // (uniform)
   const int tid = threadIdx.x;
   auto degree = [&](int i) { return deg ? deg[i] : row_ptr[i + 1] - row_ptr[i]; };
+  const bool cached = n <= kOrderCache;
   cursor[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < n; i += kScanThreads) atomicAdd(&cursor[min(degree(i), kOrderBins - 1)], 1);
+  if (cached) {
+    int d[kOrderUnroll], r[kOrderUnroll];
+#pragma unroll
+    for (int u = 0; u < kOrderUnroll; ++u) {
+      const int i = min(tid + u * kScanThreads, n - 1);
+      r[u] = row_ptr[i];
+      d[u] = deg ? deg[i] : row_ptr[i + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kOrderUnroll; ++u) {
+      const int i = tid + u * kScanThreads;
+      if (i < n) {
+        const int dd = deg ? d[u] : d[u] - r[u];
+        c_deg[i] = dd;
+        c_row[i] = r[u];
+        atomicAdd(&cursor[min(dd, kOrderBins - 1)], 1);
+      }
+    }
+  } else {
+    for (int i = tid; i < n; i += kScanThreads) atomicAdd(&cursor[min(degree(i), kOrderBins - 1)], 1);
+  }
   __syncthreads();
   // exclusive scan over the bins from the top degree down
   const int b = kOrderBins - 1 - tid;
@@ -504,9 +535,9 @@ __device__ inline void degree_order_body(const int32_t* __restrict__ deg, int n,
   cursor[b] = ex;
   __syncthreads();
   for (int i = tid; i < n; i += kScanThreads) {
-    const int d = degree(i);
+    const int d = cached ? c_deg[i] : degree(i);
     const int pos = atomicAdd(&cursor[min(d, kOrderBins - 1)], 1);
-    node_info[pos] = make_int4(i, row_ptr[i], d, 0);
+    node_info[pos] = make_int4(i, cached ? c_row[i] : row_ptr[i], d, 0);
   }
 }
 
