@@ -1,6 +1,6 @@
 """GPU parity of the HIP path against the fp64 oracle, through the C ABI.
 
-Bars: neighbour list and mask prepare bit-exact; edge harmonics within 2e-6 absolute
+Bars: neighbour list and mask prepare bit-exact; edge harmonics within 1e-6 relative
 (fp64 evaluation stored as fp32); convolution relative L2 <= 1e-5 and max |diff| <= 1e-4
 over the whole output, plus bitwise run-to-run determinism.
 """
@@ -154,14 +154,22 @@ def test_prepare_random(dev, seed, n, maxdeg, masked):
 # edge harmonics
 # ----------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "highl_768", "si_mask"])
+@pytest.mark.parametrize("name", ["tiny", "c1_768", "c2_768", "highl_768", "si_mask"])
 def test_edge_sh(dev, name):
+    """Harmonics of every edge within 1e-6 relative: per element |got - ref| <= 1e-6 |ref|
+    + 1e-12.  The library evaluates them in fp64 and stores fp32, so the error is the fp32
+    rounding of each value (relative 6e-8); the 1e-12 floor admits the fp64 evaluation's
+    own error on components that cancel to nearly zero (about 1e-16 of the l-th shell's
+    scale)."""
     wl, plan, pos, box, cell, rp, col, sh, *_ = _workload(name)
     p = C.Plan(wl.irreps_in, wl.irreps_sh, wl.l_out_max, wl.rule)
     got = C.edge_sh(p, _t(pos, dev), cell, _t(rp, dev), _t(col, dev), _t(sh, dev)).cpu().numpy()
     r = O.edge_vectors(pos, cell, rp, col, sh)
     ref = np.concatenate([O.real_sh(l, r) for l in range(plan.l_sh_max + 1)], 1)
-    assert np.abs(got - ref).max() <= 2e-6
+    err = np.abs(got.astype(np.float64) - ref)
+    worst = float((err / (np.abs(ref) + 1e-6)).max())
+    print(f"{name}: harmonics max abs {err.max():.3e}, max rel {worst:.3e}", flush=True)
+    assert np.all(err <= 1e-6 * np.abs(ref) + 1e-12)
 
 
 # ----------------------------------------------------------------------------------
