@@ -183,8 +183,8 @@ struct GroupLoad {
 // x-gradients its LDS hand-off adds).  In the forward the l <= 3 class (class 1) takes
 // groups of up to kConvJobsFwd jobs, so that one producer wave gathers each sender's
 // x_j segment (up to 7 components per channel) for all paths of its input irrep; the
-// other classes keep groups of kConvJobsBwd, as more and smaller workgroups measured
-// faster there.  Conv kernel time, groups of 3 against groups of 7: c1_768 (l <= 2)
+// other classes (and the fp64 forward) keep groups of kConvJobsBwd, as more and smaller
+// workgroups measured faster there.  Conv kernel time, groups of 3 against groups of 7: c1_768 (l <= 2)
 // 27.1 against 28.0 us; highl_768 (mostly the l >= 4 classes, whose few hundred
 // workgroups are bound by their arithmetic and edge chains) 414 against 470 us; for
 // l <= 3, c2_768 56.2 against 51.3 us and si_mask 108.3 against 105.0 us.
@@ -630,7 +630,10 @@ int cgtp_plan_create(const char* irreps_in, const char* irreps_sh, int l_out_max
   }
   P->irreps_out = format_irreps(P->out);
   for (int c = 0; c < kNumClasses; ++c) {
-    P->fwd.jobs_per_group[c] = c == 1 ? kConvJobsFwd : kConvJobsBwd;
+    // groups of 7 for the fp32 l <= 3 class only: in fp64 (K = 2, twice the lanes per
+    // channel block) groups of 3 measured faster (si_mask conv 231 -> 205 us, c5_768
+    // 247 -> 233 us; c2_768 unchanged)
+    P->fwd.jobs_per_group[c] = c == 1 && P->elem == 4 ? kConvJobsFwd : kConvJobsBwd;
     P->bwd.jobs_per_group[c] = kConvJobsBwd;
   }
   P->fwd.balance_simds = true;
