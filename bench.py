@@ -375,6 +375,10 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run a plain device copy of MIB MiB --steps times "
                          "(the reference kernel for scaling HBM byte counters)")
+    ap.add_argument("--gather-calibrate", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, gather every 5248-byte row of a MIB MiB table "
+                         "once, in a random order, --steps times (checks that the copy's counter "
+                         "scale holds for row gathers like the weight stream's)")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -395,6 +399,20 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": a.steps,
                           "read_bytes_per_copy": n, "write_bytes_per_copy": n}), flush=True)
+        return 0
+
+    if a.gather_calibrate:
+        row = 1312   # floats per row: one si_mask edge's weights
+        rows = (a.gather_calibrate << 20) // (4 * row)
+        src = torch.ones((rows, row), dtype=torch.float32, device="cuda:0")
+        idx = torch.from_numpy(np.random.default_rng(0).permutation(rows)).to("cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            torch.index_select(src, 0, idx, out=dst)
+        torch.cuda.synchronize()
+        n = rows * row * 4
+        print(json.dumps({"gather_calibration_bytes": n, "gathers": a.steps, "read_bytes_per_gather": n,
+                          "write_bytes_per_gather": n}), flush=True)
         return 0
 
     import clebsch_gordan_tensor_node_amd as C
